@@ -1,0 +1,235 @@
+"""Benchmark of the bucketed ring all-reduce on one MI355X.
+
+Headline workload: 8 virtual ranks, 1 GiB of fp32 gradient per rank
+(268,435,456 elements, drawn N(0, 1e-2) on the GPU), reduced in place by the
+fused ring-order kernel. One step = one complete all-reduce of the 8 buffers.
+Reported: bus bandwidth 2(N-1)/N * S / t (the per-rank traffic of a ring
+all-reduce), algorithm bandwidth S / t, and the HBM bandwidth of the kernel,
+2 * N * S / t, against MI355X's 8 TB/s.
+
+Beside it, in the same run: the step-by-step and persistent forms and the
+bf16 buffers of the same workload, a copy probe, the whole DDP sync of
+ResNet-50 gradients (8 ranks), the 64-rank 300M-element workload, and the CPU
+oracle timed on a sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ring all-reduce bus GB/s + HBM GB/s (% of MI355X peak), N=8, 1 GiB fp32"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_n8_1gib_fp32.json")
+KERNEL_SOURCE = os.path.join(ROOT, "ring_all_reduce_ddp_amd", "csrc", "ring_kernels.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    return ap.parse_args()
+
+
+def ensure_library():
+    from ring_all_reduce_ddp_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+
+
+def time_launches(fn, reps, torch):
+    """Mean milliseconds per call of fn() over `reps` calls, measured with HIP
+    events on torch's current stream (the stream the library launches on)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def gbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the fused kernel from the committed counter
+    profile, or None if it is missing or was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        prof = json.load(f)
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if prof.get("kernel_source_sha256") != sha:
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs its N virtual ranks on one GPU; --gpus {args.gpus} is not "
+              "supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    ensure_library()
+    import numpy as np
+    import torch
+    import ring_all_reduce_ddp_amd as rar
+    from ddp_workloads import WORKLOADS, device_ring_inputs, resnet50_param_numels
+
+    torch.cuda.set_device(0)
+    out = {}
+
+    # ------------------------------------------------------------ headline: fused, N=8, 1 GiB fp32
+    w = WORKLOADS["ring_n8_1gib"]
+    n, count = w.n, w.count
+    S = count * 4
+    bufs = device_ring_inputs(w.seed, n, count, "fp32", std=w.std)
+    # sample of the input for the CPU oracle leg: the first half of every chunk
+    L = -(-count // n)
+    half = L // 2
+    sample = [np.concatenate([t[c * L:c * L + half].cpu().numpy() for c in range(n)]) for t in bufs]
+
+    for _ in range(args.warmup):
+        rar.ring_allreduce_fused(bufs)
+    torch.cuda.synchronize()
+    ms = time_launches(lambda: rar.ring_allreduce_fused(bufs), args.steps, torch)
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rar.ddp_count_mismatches(bufs, mism)
+    torch.cuda.synchronize()
+    ranks_equal = int(mism.item()) == 0
+
+    bus = gbps(2 * (n - 1) / n * S, ms)
+    hbm_bytes = 2 * n * S
+    hbm = gbps(hbm_bytes, ms)
+    traffic = traffic_from_profile()
+
+    # ------------------------------------------------------------ same workload, other forms
+    extras = {}
+    reps = max(3, args.steps // 4)
+
+    def stepwise():
+        rar.ring_allreduce_stepwise(bufs)
+
+    def persistent():
+        rar.ring_allreduce_persistent(bufs)
+
+    step_bytes = 5 * (n - 1) * S
+    for name, fn in [("steps", stepwise), ("persistent", persistent)]:
+        fn()
+        t = time_launches(fn, reps, torch)
+        extras[name] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (n - 1) / n * S, t), 1),
+                        "hbm_gbps": round(gbps(step_bytes, t), 1),
+                        "hbm_frac_of_peak": round(gbps(step_bytes, t) / PEAK_HBM_GBPS, 4),
+                        "launches": 2 * (n - 1) if name == "steps" else 1}
+    rar.ddp_persistent_status()
+    del bufs
+    torch.cuda.empty_cache()
+
+    bb = device_ring_inputs(w.seed, n, 2 * count, "bf16", std=w.std)
+    rar.ring_allreduce_fused(bb)
+    t = time_launches(lambda: rar.ring_allreduce_fused(bb), reps, torch)
+    extras["bf16_fused"] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (n - 1) / n * S, t), 1),
+                            "hbm_gbps": round(gbps(2 * n * S, t), 1),
+                            "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4)}
+    del bb
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ copy probe (4 GiB read + 4 GiB written)
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    rar.ddp_copy_probe(dst, src)
+    t = time_launches(lambda: rar.ddp_copy_probe(dst, src), reps, torch)
+    extras["copy_probe"] = {"bytes_moved": 2 * src.numel() * 4, "ms": round(t, 4),
+                            "gbps": round(gbps(2 * src.numel() * 4, t), 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ whole DDP sync, ResNet-50, N=8
+    wr = WORKLOADS["ddp_resnet50"]
+    numels = resnet50_param_numels()
+    plan = rar.ddp_bucket_plan(numels, "fp32", world_size=wr.n)
+    arena_numel, _ = plan.grad_arena()
+    g = torch.Generator(device="cuda")
+    arenas = []
+    for r in range(wr.n):
+        g.manual_seed(1000 * wr.seed + r)
+        arenas.append(torch.randn(arena_numel, generator=g, device="cuda") * wr.std)
+    buckets = [[torch.empty(plan.bucket(b)[0], device="cuda") for _ in range(wr.n)]
+               for b in range(plan.num_buckets)]
+    sizes = [plan.bucket(b)[0] * 4 for b in range(plan.num_buckets)]
+    grad_bytes = sum(numels) * 4
+    sync = {"bucket_sizes": sizes, "params": len(numels), "grad_bytes_per_rank": grad_bytes}
+    for variant in ("fused", "steps", "persistent"):
+        rar.ddp_sync(plan, arenas, buckets, variant=variant)
+        t = time_launches(lambda: rar.ddp_sync(plan, arenas, buckets, variant=variant), reps, torch)
+        sync[variant] = {"ms": round(t, 4),
+                         "bus_gbps": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
+    extras["ddp_sync_resnet50_n8"] = sync
+    del arenas, buckets
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ 64 ranks x 300M fp32
+    w5 = WORKLOADS["ring_n64_300m"]
+    b5 = device_ring_inputs(w5.seed, w5.n, w5.count, "fp32", std=w5.std, heavy_frac=w5.heavy_frac,
+                            heavy_mult=w5.heavy_mult)
+    S5 = w5.count * 4
+    n64 = {}
+    for name, fn, nbytes, launches in [
+            ("fused", lambda: rar.ring_allreduce_fused(b5), 2 * w5.n * S5, 1),
+            ("steps", lambda: rar.ring_allreduce_stepwise(b5), 5 * (w5.n - 1) * S5, 2 * (w5.n - 1)),
+            ("persistent", lambda: rar.ring_allreduce_persistent(b5), 5 * (w5.n - 1) * S5, 1)]:
+        fn()
+        t = time_launches(fn, 2, torch)
+        n64[name] = {"ms": round(t, 3), "bus_gbps": round(gbps(2 * (w5.n - 1) / w5.n * S5, t), 1),
+                     "hbm_gbps": round(gbps(nbytes, t), 1), "launches": launches}
+    rar.ddp_persistent_status()
+    extras["ring_n64_300m"] = n64
+    del b5
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU oracle on a sample
+    from oracle import ring as oracle_ring
+    t0 = time.perf_counter()
+    oracle_ring.ring_simulate(sample, "fp32")
+    cpu_s = time.perf_counter() - t0
+    S_sample = half * n * 4
+    cpu = {"value": round(gbps(2 * (n - 1) / n * S_sample, cpu_s * 1e3), 4), "unit": "GB/s",
+           "cores": 1, "kind": "oracle",
+           "sample": (f"first half of every chunk of the same inputs: 8 ranks x {half * n} fp32 "
+                      f"elements ({S_sample / 2**20:.0f} MiB per rank), hop-by-hop numpy simulation "
+                      f"(single-threaded ufuncs), {cpu_s:.2f} s"),
+           "host_cpus_available": len(os.sched_getaffinity(0))}
+
+    line = {
+        "metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (N(0, 1e-2) per rank, seeded on the GPU)",
+        "config": {"workload": "ring_n8_1gib", "virtual_ranks": n, "elements_per_rank": count,
+                   "bytes_per_rank": S, "variant": "fused", "in_place": True},
+        "algbw_gbps": round(gbps(S, ms), 2), "busbw_gbps": round(bus, 2), "hbm_gbps": round(hbm, 1),
+        "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4), "ranks_equal_after": ranks_equal,
+        "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": hbm_bytes},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * ddp_ring.h -- C ABI of the MI355X (gfx950) bucketed ring all-reduce of DDP
+ * gradients over N virtual ranks whose buffers all live in one GPU's HBM.
+ *
+ * The operations follow three pages:
+ *   [R]  "DDP 与 Ring All-Reduce" (blog.vllbc.top/visual-reading/ddp-ring-allreduce),
+ *        sections 03 (two phases, buckets, overlap), 04 (traffic), 05 (step timing);
+ *   [D]  "Day 17 数据并行 DP/DDP" (blog.ans20xx.com/posts/ai/day17),
+ *        parts "bucket 与 overlap" and "源码阅读路线";
+ *   [X]  "DDP 与 Ring-AllReduce" (xuesongtap.github.io/2025/09/06/ddp.html),
+ *        §1.3.1 and the worked example of §1.3.2.
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns DDP_OK (0) or a negative status; on failure
+ *     ddp_last_error() gives a message for the calling thread. No C++
+ *     exception crosses this boundary.
+ *   - "device pointer" means memory from hipMalloc (or an allocator built on
+ *     it, such as PyTorch's caching allocator) on the current HIP device.
+ *     The library checks, with hipMemGetAddressRange, that every byte range it
+ *     will touch lies inside one allocation, and that buffers written by one
+ *     call do not overlap; a failed check returns DDP_EINVAL before anything
+ *     is launched.
+ *   - Arrays of device pointers (bufs, grad_arenas, bucket_bufs) are HOST
+ *     arrays; the library copies them into the kernel arguments.
+ *   - All device memory belongs to the caller. The library allocates only
+ *     small tables of its own: per plan, a device copy of the bucket layout
+ *     (made on the first pack/unpack on a device, freed by ddp_plan_free), and
+ *     per device, a few KiB of barrier and status words (kept until the process
+ *     ends).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without waiting; completion follows stream order,
+ *     the analogue of waiting on the collective's work handle ([D], "源码阅读路线").
+ *   - Chunking ([R] section 03; [X] §1.3.2.1): a buffer of `count` elements is
+ *     cut into N chunks of L = ceil(count / N) elements; chunk c covers
+ *     [c*L, min((c+1)*L, count)) and may be short or empty. In reduce-scatter
+ *     step s rank r passes chunk (r-1-s) mod N to rank (r+1) mod N, which adds
+ *     it into its own copy, rounded once to the buffer dtype (nearest, ties to
+ *     even, subnormals kept); in all-gather step s rank r passes chunk
+ *     (r-s) mod N and the receiver overwrites its copy. Chunk c therefore
+ *     starts at rank c+1 and ends fully reduced on rank c ([X] §1.3.2.1).
+ *   - N (the world size) lies in [1, DDP_MAX_RANKS]. Buffers are in place:
+ *     rank r's buffer is read and overwritten.
+ *   - Concurrency: calls may be issued from several host threads. Calls
+ *     enqueued on different streams must not touch the same buffers at the
+ *     same time (as with any kernels).
+ */
+#ifndef DDP_RING_H
+#define DDP_RING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDP_MAX_RANKS 64
+
+/* status codes */
+#define DDP_OK 0
+#define DDP_EINVAL (-1)       /* bad argument; nothing was launched */
+#define DDP_EHIP (-2)         /* a HIP runtime call failed; message has hipGetErrorString */
+#define DDP_ENORESOURCE (-3)  /* the persistent grid cannot be made co-resident */
+#define DDP_ETIMEOUT (-4)     /* a persistent grid barrier gave up waiting */
+#define DDP_ENOMEM (-5)       /* a host or device allocation of the library failed */
+
+/* buffer element types */
+#define DDP_FP32 0            /* IEEE binary32, 4 bytes */
+#define DDP_BF16 1            /* bfloat16, 2 bytes: the upper half of a binary32 */
+
+/* ring phases ([R] section 03) */
+#define DDP_RS 0              /* reduce-scatter: add the received chunk */
+#define DDP_AG 1              /* all-gather: overwrite with the received chunk */
+
+/* all-reduce variants for ddp_sync */
+#define DDP_VARIANT_FUSED 0
+#define DDP_VARIANT_STEPS 1
+#define DDP_VARIANT_PERSISTENT 2
+
+typedef struct ddp_plan ddp_plan; /* opaque; host memory owned by the library */
+
+/* Message describing the last failure of the calling thread ("" if none). */
+const char* ddp_last_error(void);
+
+/* ---------------------------------------------------------------- planner
+ * ddp_bucket_plan: assign parameters to flat buckets ([R] section 03, parts
+ * "Bucket" and "Overlap"; [D] "bucket 与 overlap").
+ *   param_numels[n_params]: element counts in registration order (host array;
+ *       each >= 0; n_params >= 0).
+ *   dtype: DDP_FP32 or DDP_BF16 (the gradients' and the buckets' type).
+ *   cap_bytes: capacity of every bucket after the first (> 0; 25 MiB =
+ *       26214400 is DDP's default); first_bucket_bytes: capacity of bucket 0
+ *       (> 0; 1 MiB = 1048576 is DDP's default).
+ *   world_size: N, used to pad each bucket.
+ *   *out receives a new plan, to be released with ddp_plan_free.
+ * Rules: parameters are taken in reverse registration order; a parameter
+ * that would push the open bucket past its capacity opens the next bucket; a
+ * parameter larger than the capacity has a bucket of its own. With
+ * V = 16 / element size, each member starts at a multiple of V elements and
+ * takes round_up(numel, V) elements; a bucket's length is padded with zeros
+ * to a multiple of N*V elements, so its N ring chunks are equal and start on
+ * 16-byte boundaries. Buckets are numbered in launch order; every rank uses
+ * the same plan and order.
+ */
+int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, int32_t dtype,
+                    int64_t cap_bytes, int64_t first_bucket_bytes, int32_t world_size,
+                    ddp_plan** out);
+
+/* Releases a plan and its device tables (NULL is accepted). Must not be
+ * called while work that uses the plan is still running. */
+void ddp_plan_free(ddp_plan* plan);
+
+/* Number of buckets. */
+int ddp_plan_num_buckets(const ddp_plan* plan, int32_t* out);
+
+/* Bucket b's padded length in elements and its number of members. */
+int ddp_plan_bucket(const ddp_plan* plan, int32_t b, int64_t* padded_numel, int32_t* n_members);
+
+/* Member i of bucket b: parameter index, offset in the bucket (elements) and
+ * element count. Members are listed in bucket order (reverse parameter order). */
+int ddp_plan_member(const ddp_plan* plan, int32_t b, int32_t i, int32_t* param_idx,
+                    int64_t* offset, int64_t* numel);
+
+/* Layout of a rank's gradient arena: all parameters' gradients in
+ * registration order, parameter p starting at param_offsets[p] elements (a
+ * multiple of V, i.e. 16-byte aligned). Writes *arena_numel and, if
+ * param_offsets is not NULL, n_params offsets into the host array. */
+int ddp_plan_grad_arena(const ddp_plan* plan, int64_t* arena_numel, int64_t* param_offsets);
+
+/* ---------------------------------------------------------------- pack / unpack
+ * bucket_pack: copy gradients into bucket b's flat buffer on every rank
+ * (the gradient-to-bucket copy of DDP's default gradient_as_bucket_view=False,
+ * [R] sections 03 and 05).
+ *   grad_arenas[N]: device pointers, 16-byte aligned, each holding one rank's
+ *       arena as laid out by ddp_plan_grad_arena (arena_numel elements).
+ *   bucket_bufs[N]: device pointers, 16-byte aligned, each padded_numel
+ *       elements of bucket b; positions not covered by a member are zeroed.
+ *   N must equal the plan's world size.
+ */
+int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* grad_arenas,
+                void* const* bucket_bufs, int32_t N, void* stream);
+
+/* bucket_unpack_scale: copy bucket b back into every rank's gradients,
+ * multiplying each element by `scale` (fp32) with one rounding to the dtype:
+ * grad = rnd(scale * bucket). scale = 1/N turns the ring's sum into DDP's mean
+ * ([R] section 05, step 3; [D] "源码阅读路线": divide by the world size, then
+ * copy back). For N a power of two this equals division by N bit for bit.
+ * Arguments as for bucket_pack; only members' elements are written. */
+int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs,
+                        void* const* grad_arenas, int32_t N, float scale, void* stream);
+
+/* ---------------------------------------------------------------- ring all-reduce
+ * bufs[N]: device pointers to the N rank buffers, `count` elements of `dtype`
+ * each, aligned to the element size, pairwise disjoint. count >= 0.
+ */
+
+/* One step of the ring ([R] section 03; [X] §1.3.2.1 / §1.3.2.2): all N
+ * (rank r -> rank r+1) transfers of `step` in `phase`, in one launch.
+ * phase = DDP_RS: buf[r+1][chunk (r-1-step) mod N] += buf[r][same chunk];
+ * phase = DDP_AG: buf[r+1][chunk (r-step) mod N]  = buf[r][same chunk].
+ * step in [0, N-2]. A full all-reduce is RS steps 0..N-2 then AG steps
+ * 0..N-2, in order on one stream: 2(N-1) launches ([X] §1.3.1). */
+int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                        int32_t step, int32_t phase, void* stream);
+
+/* The first n_steps of the 2(N-1) steps (RS steps first, then AG steps) in
+ * one cooperative launch, with a grid-wide barrier between consecutive
+ * steps. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce.
+ * Returns DDP_ENORESOURCE if the grid cannot be co-resident. A barrier that
+ * waits longer than its bound (seconds) lets every block exit and records a
+ * sticky flag read by ddp_persistent_status. */
+int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                              int32_t n_steps, void* stream);
+
+/* Waits for `stream`, then reports DDP_ETIMEOUT if any persistent launch on
+ * the current device timed out since the last call (and clears the flag). */
+int ddp_persistent_status(void* stream);
+
+/* The whole all-reduce in one pass: every element is read once from each of
+ * the N ranks, summed in the exact order the ring adds it (chunk c's sum
+ * starts with rank c+1 and adds ranks c+2, ..., c, one rounding per add) and
+ * written to all N ranks. The final state is bit-identical to the 2(N-1)
+ * steps; the HBM traffic is 2*N*count*element bytes instead of
+ * 5*(N-1)*count*element. */
+int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                         void* stream);
+
+/* ---------------------------------------------------------------- whole sync
+ * ddp_sync: one DDP gradient synchronisation. For every bucket b in plan
+ * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_*) on
+ * bucket b's N buffers, bucket_unpack_scale with `scale` (pass 1/N for DDP's
+ * mean). Bucket i+1 is never started before bucket i ([R] section 03).
+ *   grad_arenas[N]: as for bucket_pack.
+ *   bucket_bufs[B*N]: bucket b of rank r at index b*N + r (host array).
+ */
+int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs,
+             int32_t N, int32_t variant, float scale, void* stream);
+
+/* ---------------------------------------------------------------- checks and probes
+ * ddp_count_mismatches: *out_dev (a device uint64, overwritten) receives the
+ * number of element positions at which some rank's bits differ from rank 0's
+ * (0 after a complete all-reduce, [X] §1.3.2.2). */
+int ddp_count_mismatches(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                         uint64_t* out_dev, void* stream);
+
+/* ddp_copy_probe: copies nbytes (a multiple of 16) from src to dst with 16-byte
+ * vector loads and stores: a same-run reference for achievable HBM bandwidth
+ * and for scaling memory-traffic counters. */
+int ddp_copy_probe(void* dst, const void* src, int64_t nbytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDP_RING_H */

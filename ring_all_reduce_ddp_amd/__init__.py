@@ -1,0 +1,271 @@
+"""Python binding of libddp_ring.so: the bucketed ring all-reduce of DDP
+gradients over N virtual ranks on one MI355X.
+
+The functions have the names of the C entry points in include/ddp_ring.h and
+only marshal arguments: torch tensors become device pointers, dtypes become
+DDP_FP32 / DDP_BF16, and the stream defaults to torch's current stream. Every
+step of the computation runs in the library's HIP kernels; there is no other
+code path. Importing this module fails if the library has not been built
+(python -m ring_all_reduce_ddp_amd.build).
+
+PyTorch is used for device memory and streams only. It is imported before the
+library is loaded so that both use the single HIP runtime that torch ships.
+"""
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libddp_ring.so")
+
+DDP_OK = 0
+DDP_EINVAL = -1
+DDP_EHIP = -2
+DDP_ENORESOURCE = -3
+DDP_ETIMEOUT = -4
+DDP_ENOMEM = -5
+DDP_FP32 = 0
+DDP_BF16 = 1
+DDP_RS = 0
+DDP_AG = 1
+DDP_MAX_RANKS = 64
+VARIANTS = {"fused": 0, "steps": 1, "persistent": 2}
+
+_STATUS_NAMES = {DDP_EINVAL: "DDP_EINVAL", DDP_EHIP: "DDP_EHIP", DDP_ENORESOURCE: "DDP_ENORESOURCE",
+                 DDP_ETIMEOUT: "DDP_ETIMEOUT", DDP_ENOMEM: "DDP_ENOMEM"}
+
+
+class DDPError(RuntimeError):
+    """A non-zero status from the library, with ddp_last_error()'s message."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m ring_all_reduce_ddp_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "ddp_last_error": (ctypes.c_char_p, []),
+        "ddp_bucket_plan": (ctypes.c_int, [ctypes.POINTER(i64), i32, i32, i64, i64, i32,
+                                           ctypes.POINTER(vp)]),
+        "ddp_plan_free": (None, [vp]),
+        "ddp_plan_num_buckets": (ctypes.c_int, [vp, ctypes.POINTER(i32)]),
+        "ddp_plan_bucket": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]),
+        "ddp_plan_member": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                           ctypes.POINTER(i64)]),
+        "ddp_plan_grad_arena": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "bucket_pack": (ctypes.c_int, [vp, i32, pp, pp, i32, vp]),
+        "bucket_unpack_scale": (ctypes.c_int, [vp, i32, pp, pp, i32, f32, vp]),
+        "ring_allreduce_step": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, vp]),
+        "ring_allreduce_persistent": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
+        "ddp_persistent_status": (ctypes.c_int, [vp]),
+        "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
+        "ddp_sync": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, vp]),
+        "ddp_count_mismatches": (ctypes.c_int, [pp, i32, i64, i32, vp, vp]),
+        "ddp_copy_probe": (ctypes.c_int, [vp, vp, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != DDP_OK:
+        msg = lib.ddp_last_error()
+        raise DDPError(status, msg.decode() if msg else "")
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+_TORCH_DTYPES = {torch.float32: DDP_FP32, torch.bfloat16: DDP_BF16}
+_NAMED_DTYPES = {"fp32": DDP_FP32, "bf16": DDP_BF16, DDP_FP32: DDP_FP32, DDP_BF16: DDP_BF16}
+
+
+def dtype_code(dtype):
+    if dtype in _TORCH_DTYPES:
+        return _TORCH_DTYPES[dtype]
+    if dtype in _NAMED_DTYPES:
+        return _NAMED_DTYPES[dtype]
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _ptr(x):
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _ptr_array(xs):
+    return (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ring_args(bufs, count, dtype):
+    """(pointer array, N, count, dtype code) from tensors or raw pointers."""
+    n = len(bufs)
+    if isinstance(bufs[0], torch.Tensor):
+        t0 = bufs[0]
+        if dtype is None:
+            dtype = t0.dtype
+        if count is None:
+            count = t0.numel()
+        for t in bufs:
+            if not t.is_contiguous() or t.numel() < count or t.dtype != t0.dtype:
+                raise ValueError("rank buffers must be contiguous tensors of one dtype holding count elements")
+    if count is None or dtype is None:
+        raise ValueError("count and dtype are required for raw pointers")
+    return _ptr_array(bufs), n, int(count), dtype_code(dtype)
+
+
+# ---------------------------------------------------------------- planner
+
+class Plan:
+    """A bucket plan (see ddp_bucket_plan). Owns the library's handle."""
+
+    def __init__(self, handle, n_params, dtype, world_size):
+        self._h = handle
+        self.n_params = n_params
+        self.dtype = dtype
+        self.world_size = world_size
+
+    @property
+    def handle(self):
+        return self._h
+
+    def free(self):
+        if self._h:
+            lib.ddp_plan_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    @property
+    def num_buckets(self):
+        n = ctypes.c_int32()
+        _check(lib.ddp_plan_num_buckets(self._h, ctypes.byref(n)))
+        return n.value
+
+    def bucket(self, b):
+        """(padded_numel, [(param_index, offset, numel), ...]) of bucket b."""
+        padded, nm = ctypes.c_int64(), ctypes.c_int32()
+        _check(lib.ddp_plan_bucket(self._h, b, ctypes.byref(padded), ctypes.byref(nm)))
+        members = []
+        for i in range(nm.value):
+            p, off, m = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+            _check(lib.ddp_plan_member(self._h, b, i, ctypes.byref(p), ctypes.byref(off), ctypes.byref(m)))
+            members.append((p.value, off.value, m.value))
+        return padded.value, members
+
+    def buckets(self):
+        """All buckets as dicts {"members": [...], "padded_numel": int}."""
+        out = []
+        for b in range(self.num_buckets):
+            padded, members = self.bucket(b)
+            out.append({"members": members, "padded_numel": padded})
+        return out
+
+    def grad_arena(self):
+        """(arena_numel, [offset of parameter p in elements])."""
+        n = ctypes.c_int64()
+        offs = (ctypes.c_int64 * max(self.n_params, 1))()
+        _check(lib.ddp_plan_grad_arena(self._h, ctypes.byref(n), offs))
+        return n.value, list(offs[:self.n_params])
+
+
+def ddp_bucket_plan(param_numels, dtype="fp32", cap_bytes=25 * 1024 * 1024,
+                    first_bucket_bytes=1024 * 1024, world_size=1):
+    numels = (ctypes.c_int64 * max(len(param_numels), 1))(*[int(m) for m in param_numels])
+    h = ctypes.c_void_p()
+    _check(lib.ddp_bucket_plan(numels, len(param_numels), dtype_code(dtype), int(cap_bytes),
+                               int(first_bucket_bytes), int(world_size), ctypes.byref(h)))
+    return Plan(h.value, len(param_numels), dtype_code(dtype), int(world_size))
+
+
+# ---------------------------------------------------------------- kernels
+
+def bucket_pack(plan, b, grad_arenas, bucket_bufs, stream=None):
+    _check(lib.bucket_pack(plan.handle, b, _ptr_array(grad_arenas), _ptr_array(bucket_bufs),
+                           len(bucket_bufs), _stream(stream)))
+
+
+def bucket_unpack_scale(plan, b, bucket_bufs, grad_arenas, scale, stream=None):
+    _check(lib.bucket_unpack_scale(plan.handle, b, _ptr_array(bucket_bufs), _ptr_array(grad_arenas),
+                                   len(bucket_bufs), float(scale), _stream(stream)))
+
+
+def ring_allreduce_step(bufs, step, phase, count=None, dtype=None, stream=None):
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    _check(lib.ring_allreduce_step(ptrs, n, count, dt, int(step), int(phase), _stream(stream)))
+
+
+def ring_allreduce_stepwise(bufs, count=None, dtype=None, stream=None):
+    """The whole all-reduce as 2(N-1) ring_allreduce_step launches, in order."""
+    n = len(bufs)
+    for phase in (DDP_RS, DDP_AG):
+        for s in range(n - 1):
+            ring_allreduce_step(bufs, s, phase, count, dtype, stream)
+
+
+def ring_allreduce_persistent(bufs, n_steps=None, count=None, dtype=None, stream=None):
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    if n_steps is None:
+        n_steps = 2 * (n - 1)
+    _check(lib.ring_allreduce_persistent(ptrs, n, count, dt, int(n_steps), _stream(stream)))
+
+
+def ddp_persistent_status(stream=None):
+    _check(lib.ddp_persistent_status(_stream(stream)))
+
+
+def ring_allreduce_fused(bufs, count=None, dtype=None, stream=None):
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    _check(lib.ring_allreduce_fused(ptrs, n, count, dt, _stream(stream)))
+
+
+def ddp_sync(plan, grad_arenas, bucket_bufs, variant="fused", scale=None, stream=None):
+    """bucket_bufs: list over buckets of lists over ranks (or a flat list,
+    bucket-major)."""
+    flat = [x for row in bucket_bufs for x in row] if isinstance(bucket_bufs[0], (list, tuple)) \
+        else list(bucket_bufs)
+    n = len(grad_arenas)
+    if scale is None:
+        scale = 1.0 / n
+    _check(lib.ddp_sync(plan.handle, _ptr_array(grad_arenas), _ptr_array(flat), n,
+                        VARIANTS[variant], float(scale), _stream(stream)))
+
+
+def ddp_count_mismatches(bufs, out, count=None, dtype=None, stream=None):
+    """Enqueues the count into `out` (a device int64/uint64 tensor of one element)."""
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    _check(lib.ddp_count_mismatches(ptrs, n, count, dt, ctypes.c_void_p(_ptr(out)), _stream(stream)))
+
+
+def ddp_copy_probe(dst, src, nbytes=None, stream=None):
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    _check(lib.ddp_copy_probe(ctypes.c_void_p(_ptr(dst)), ctypes.c_void_p(_ptr(src)), int(nbytes),
+                              _stream(stream)))

@@ -1,0 +1,80 @@
+// Internal declarations shared by the host planner and the HIP launchers.
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ddp_ring.h"
+
+namespace ddp {
+
+constexpr int kVectorBytes = 16;
+
+inline int elem_bytes(int32_t dtype) { return dtype == DDP_BF16 ? 2 : 4; }
+inline bool valid_dtype(int32_t dtype) { return dtype == DDP_FP32 || dtype == DDP_BF16; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Records `msg` as the calling thread's last error and returns `status`.
+int fail(int status, const std::string& msg);
+void clear_error();
+
+// One contiguous piece of a bucket: a member's slot (numel elements copied,
+// the rest of the slot zero) or the tail padding (numel == 0).
+struct Segment {
+  int64_t dst_off;     // offset in the bucket, elements (multiple of V)
+  int64_t src_off;     // offset in the gradient arena, elements (multiple of V)
+  int64_t numel;       // elements that come from the gradient
+  int64_t slot;        // elements of the bucket covered (multiple of V)
+  int64_t tile_begin;  // first pack tile of this segment (prefix sum)
+};
+
+struct Member {
+  int32_t param;
+  int64_t offset;
+  int64_t numel;
+};
+
+struct Bucket {
+  std::vector<Member> members;
+  int64_t padded_numel = 0;
+  int64_t seg_begin = 0;   // index of its first segment in plan.segments
+  int64_t n_segs = 0;
+  int64_t n_tiles = 0;     // pack/unpack tiles per rank
+};
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceTable {
+  Segment* segs = nullptr;   // device copy of plan.segments
+};
+
+}  // namespace ddp
+
+struct ddp_plan {
+  int32_t dtype = DDP_FP32;
+  int32_t world_size = 1;
+  int64_t cap_bytes = 0;
+  int64_t first_bucket_bytes = 0;
+  std::vector<int64_t> numels;          // registration order
+  std::vector<int64_t> arena_offsets;   // registration order, elements
+  int64_t arena_numel = 0;
+  std::vector<ddp::Bucket> buckets;
+  std::vector<ddp::Segment> segments;   // all buckets' segments, bucket-major
+  int64_t tile_elems = 0;               // elements per pack tile
+  std::mutex mu;                        // guards `device`
+  ddp::DeviceTable device[ddp::kMaxDevices];
+};
+
+namespace ddp {
+// Elements covered by one pack/unpack tile; fixed when the plan is built so
+// the tile prefix sums in the segments match the kernels.
+constexpr int kPackThreads = 256;
+constexpr int kPackVecsPerThread = 4;
+inline int64_t pack_tile_elems(int32_t dtype) {
+  return int64_t(kPackThreads) * kPackVecsPerThread * (kVectorBytes / elem_bytes(dtype));
+}
+// Releases the device tables of a plan (defined with the HIP code).
+void release_device_tables(ddp_plan* plan);
+}  // namespace ddp

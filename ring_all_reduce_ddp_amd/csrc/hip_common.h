@@ -1,0 +1,170 @@
+// Device-side helpers and host-side launch checks shared by the HIP sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "ddp_internal.h"
+
+namespace ddp {
+
+// A 16-byte vector of four 32-bit words (a clang vector type, so the
+// non-temporal load/store builtins accept it).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // threads per block of every streaming kernel (4 waves of 64)
+
+// The N rank base pointers, passed by value in the kernel arguments (512 bytes).
+struct RankPtrs {
+  void* p[DDP_MAX_RANKS];
+};
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Returns DDP_EHIP with the runtime's message if `e` is an error.
+inline int hip_fail(hipError_t e, const char* where) {
+  return fail(DDP_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define DDP_HIP_TRY(expr, where)                       \
+  do {                                                 \
+    hipError_t _e = (expr);                            \
+    if (_e != hipSuccess) return ::ddp::hip_fail(_e, where); \
+  } while (0)
+
+// Host-side checks (defined in runtime.hip).
+// Every byte of [p, p + bytes) must lie inside one device allocation.
+int check_range(const void* p, int64_t bytes, const char* fn, const char* what);
+// N rank buffers of `bytes` each: non-NULL, aligned to `align`, inside their
+// allocations and pairwise disjoint.
+int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, const char* fn,
+                       const char* what);
+// True if every pointer is 16-byte aligned.
+bool all_aligned16(void* const* bufs, int32_t n);
+
+// Per-device persistent-barrier words (defined in runtime.hip): *slot receives
+// a device pointer to kSlotWords 32-bit words reserved for one launch, zeroed
+// on `stream` ahead of it; *status the device's sticky timeout word.
+int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status);
+
+// ---------------------------------------------------------------- device helpers
+
+// Round an fp32 value to the nearest bf16 (ties to even) and return the bf16
+// as an fp32 value with its low 16 bits clear. NaN stays a quiet NaN.
+__device__ __forceinline__ float round_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return __uint_as_float((u | 0x00400000u) & 0xffff0000u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xffff0000u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// Per-dtype arithmetic on 16-byte vectors and on single elements. An
+// accumulator holds values of the buffer dtype (bf16 values are kept as fp32
+// numbers with the low 16 bits clear); every add is rounded once to the dtype.
+template <int DT>
+struct Ops;
+
+template <>
+struct Ops<DDP_FP32> {
+  static constexpr int V = 4;  // elements per 16-byte vector
+  using scalar_t = float;
+  struct Acc {
+    float v[4];
+  };
+  static __device__ __forceinline__ Acc from(u32x4 w) {
+    return Acc{{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                __uint_as_float(w.w)}};
+  }
+  static __device__ __forceinline__ void add(Acc& a, u32x4 w) {
+    a.v[0] += __uint_as_float(w.x);
+    a.v[1] += __uint_as_float(w.y);
+    a.v[2] += __uint_as_float(w.z);
+    a.v[3] += __uint_as_float(w.w);
+  }
+  static __device__ __forceinline__ u32x4 to(const Acc& a) {
+    return u32x4{__float_as_uint(a.v[0]), __float_as_uint(a.v[1]), __float_as_uint(a.v[2]),
+                 __float_as_uint(a.v[3])};
+  }
+  static __device__ __forceinline__ u32x4 scale(u32x4 w, float s) {
+    return u32x4{__float_as_uint(__uint_as_float(w.x) * s), __float_as_uint(__uint_as_float(w.y) * s),
+                 __float_as_uint(__uint_as_float(w.z) * s), __float_as_uint(__uint_as_float(w.w) * s)};
+  }
+  // single elements
+  static __device__ __forceinline__ float load1(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+  static __device__ __forceinline__ float add1(float a, float b) { return a + b; }
+  static __device__ __forceinline__ float mul1(float a, float s) { return a * s; }
+};
+
+template <>
+struct Ops<DDP_BF16> {
+  static constexpr int V = 8;
+  using scalar_t = float;  // the bf16 value as an fp32 number
+  struct Acc {
+    float v[8];
+  };
+  static __device__ __forceinline__ Acc from(u32x4 w) {
+    return Acc{{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bf16_lo(w.z),
+                bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)}};
+  }
+  static __device__ __forceinline__ void add(Acc& a, u32x4 w) {
+    a.v[0] = round_bf16(a.v[0] + bf16_lo(w.x));
+    a.v[1] = round_bf16(a.v[1] + bf16_hi(w.x));
+    a.v[2] = round_bf16(a.v[2] + bf16_lo(w.y));
+    a.v[3] = round_bf16(a.v[3] + bf16_hi(w.y));
+    a.v[4] = round_bf16(a.v[4] + bf16_lo(w.z));
+    a.v[5] = round_bf16(a.v[5] + bf16_hi(w.z));
+    a.v[6] = round_bf16(a.v[6] + bf16_lo(w.w));
+    a.v[7] = round_bf16(a.v[7] + bf16_hi(w.w));
+  }
+  static __device__ __forceinline__ u32x4 to(const Acc& a) {
+    return u32x4{bf16_pack(a.v[0], a.v[1]), bf16_pack(a.v[2], a.v[3]), bf16_pack(a.v[4], a.v[5]),
+                 bf16_pack(a.v[6], a.v[7])};
+  }
+  static __device__ __forceinline__ uint32_t scale2(uint32_t w, float s) {
+    return bf16_pack(round_bf16(bf16_lo(w) * s), round_bf16(bf16_hi(w) * s));
+  }
+  static __device__ __forceinline__ u32x4 scale(u32x4 w, float s) {
+    return u32x4{scale2(w.x, s), scale2(w.y, s), scale2(w.z, s), scale2(w.w, s)};
+  }
+  static __device__ __forceinline__ float load1(const void* p, int64_t i) {
+    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  static __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = uint16_t(__float_as_uint(v) >> 16);
+  }
+  static __device__ __forceinline__ float add1(float a, float b) { return round_bf16(a + b); }
+  static __device__ __forceinline__ float mul1(float a, float s) { return round_bf16(a * s); }
+};
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
+}
+
+}  // namespace ddp

@@ -1,0 +1,242 @@
+// Gradient <-> bucket copies of a DDP sync, and the whole sync.
+//
+// Page "DDP 与 Ring All-Reduce" (blog.vllbc.top), sections 03 and 05: with
+// DDP's default gradient_as_bucket_view=False the gradients are copied into
+// each bucket's flat buffer before its all-reduce, and the reduced bucket is
+// copied back into every parameter's .grad; the reducer divides the summed
+// gradient by the world size. Page "Day 17 数据并行 DP/DDP" (blog.ans20xx.com),
+// part "源码阅读路线": after a bucket's all-reduce completes it is divided by
+// the world size and copied back. Here the division is a multiplication by
+// the caller's fp32 `scale` (1/N), fused into the copy back.
+//
+// A bucket is a list of segments (each member's slot, then the zero padding);
+// each segment is covered by whole tiles so a block never mixes segments, and
+// a block finds its segment by a uniform binary search over the tile prefix
+// sums. Members and arena offsets start on 16-byte boundaries, so everything
+// but the last partial vector of a member moves as 16-byte vectors.
+#include <algorithm>
+
+#include "hip_common.h"
+
+namespace ddp {
+namespace {
+
+__device__ __forceinline__ int find_segment(const Segment* segs, int n_segs, int64_t tile) {
+  int lo = 0, hi = n_segs - 1;  // last segment whose tile_begin <= tile
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].tile_begin <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, int n_segs, int64_t n_tiles,
+                                                   RankPtrs arenas, RankPtrs buckets) {
+  using O = Ops<DT>;
+  constexpr int V = O::V;
+  constexpr int U = kPackVecsPerThread;
+  constexpr int64_t kTile = int64_t(kThreads) * U * V;
+  const void* arena = arenas.p[blockIdx.y];
+  void* bucket = buckets.p[blockIdx.y];
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const int64_t first = (tile - sg.tile_begin) * kTile;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;  // element in the slot
+      if (e >= sg.slot) continue;
+      u32x4* d = static_cast<u32x4*>(bucket) + (sg.dst_off + e) / V;
+      if (e + V <= sg.numel) {
+        *d = static_cast<const u32x4*>(arena)[(sg.src_off + e) / V];
+      } else if (e >= sg.numel) {
+        *d = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        for (int i = 0; i < V; ++i)
+          O::store1(bucket, sg.dst_off + e + i, e + i < sg.numel ? O::load1(arena, sg.src_off + e + i) : 0.0f);
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, int n_segs, int64_t n_tiles,
+                                                           RankPtrs buckets, RankPtrs arenas, float scale) {
+  using O = Ops<DT>;
+  constexpr int V = O::V;
+  constexpr int U = kPackVecsPerThread;
+  constexpr int64_t kTile = int64_t(kThreads) * U * V;
+  const void* bucket = buckets.p[blockIdx.y];
+  void* arena = arenas.p[blockIdx.y];
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const int64_t first = (tile - sg.tile_begin) * kTile;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e >= sg.numel) continue;  // padding and slack stay in the bucket
+      if (e + V <= sg.numel) {
+        const u32x4 x = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
+        static_cast<u32x4*>(arena)[(sg.src_off + e) / V] = O::scale(x, scale);
+      } else {
+        for (int64_t i = e; i < sg.numel; ++i)
+          O::store1(arena, sg.src_off + i, O::mul1(O::load1(bucket, sg.dst_off + i), scale));
+      }
+    }
+  }
+}
+
+// Device copy of the plan's segments on the current device (made once).
+int device_segments(ddp_plan* plan, const Segment** out) {
+  int dev = 0;
+  DDP_HIP_TRY(hipGetDevice(&dev), "plan tables: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "plan tables: device index beyond 64");
+  std::lock_guard<std::mutex> lock(plan->mu);
+  DeviceTable& t = plan->device[dev];
+  if (t.segs == nullptr && !plan->segments.empty()) {
+    const size_t bytes = sizeof(Segment) * plan->segments.size();
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DDP_ENOMEM, std::string("plan tables: hipMalloc: ") + hipGetErrorString(e));
+    }
+    e = hipMemcpy(p, plan->segments.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "plan tables: hipMemcpy");
+    }
+    t.segs = static_cast<Segment*>(p);
+  }
+  *out = t.segs;
+  return DDP_OK;
+}
+
+bool spans_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return abytes > 0 && bbytes > 0 && x < y + uint64_t(bbytes) && y < x + uint64_t(abytes);
+}
+
+// Checks shared by pack and unpack.
+int check_copy(const char* fn, const ddp_plan* plan, int32_t b, const void* const* arenas,
+               const void* const* buckets, int32_t N) {
+  if (plan == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": plan is NULL");
+  if (b < 0 || b >= int32_t(plan->buckets.size()))
+    return fail(DDP_EINVAL, std::string(fn) + ": bucket index out of range");
+  if (N != plan->world_size)
+    return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
+  const int eb = elem_bytes(plan->dtype);
+  const int64_t abytes = plan->arena_numel * eb;
+  const int64_t bbytes = plan->buckets[b].padded_numel * eb;
+  int st = check_rank_buffers(const_cast<void* const*>(arenas), N, abytes, 16, fn, "grad_arenas");
+  if (st != DDP_OK) return st;
+  st = check_rank_buffers(const_cast<void* const*>(buckets), N, bbytes, 16, fn, "bucket_bufs");
+  if (st != DDP_OK) return st;
+  for (int i = 0; i < N; ++i)
+    for (int j = 0; j < N; ++j)
+      if (spans_overlap(arenas[i], abytes, buckets[j], bbytes))
+        return fail(DDP_EINVAL, std::string(fn) + ": grad_arenas[" + std::to_string(i) +
+                                    "] overlaps bucket_bufs[" + std::to_string(j) + "]");
+  return DDP_OK;
+}
+
+unsigned copy_grid(int64_t tiles) { return unsigned(std::max<int64_t>(1, std::min<int64_t>(tiles, 1 << 16))); }
+
+}  // namespace
+
+void release_device_tables(ddp_plan* plan) {
+  std::lock_guard<std::mutex> lock(plan->mu);
+  for (DeviceTable& t : plan->device) {
+    if (t.segs != nullptr) {
+      (void)hipFree(t.segs);
+      t.segs = nullptr;
+    }
+  }
+}
+
+}  // namespace ddp
+
+using namespace ddp;
+
+extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* grad_arenas,
+                           void* const* bucket_bufs, int32_t N, void* stream) {
+  const char* fn = "bucket_pack";
+  int st = check_copy(fn, plan, b, grad_arenas, bucket_bufs, N);
+  if (st != DDP_OK) return st;
+  const Bucket& bk = plan->buckets[b];
+  if (bk.n_tiles == 0) return DDP_OK;
+  const Segment* segs = nullptr;
+  st = device_segments(const_cast<ddp_plan*>(plan), &segs);
+  if (st != DDP_OK) return st;
+  RankPtrs A{}, B{};
+  for (int r = 0; r < N; ++r) {
+    A.p[r] = const_cast<void*>(grad_arenas[r]);
+    B.p[r] = bucket_bufs[r];
+  }
+  const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
+  hipStream_t s = as_stream(stream);
+  if (plan->dtype == DDP_FP32)
+    hipLaunchKernelGGL(k_pack<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+  else
+    hipLaunchKernelGGL(k_pack<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+  DDP_HIP_TRY(hipGetLastError(), "bucket_pack: launch");
+  return DDP_OK;
+}
+
+extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs,
+                                   void* const* grad_arenas, int32_t N, float scale, void* stream) {
+  const char* fn = "bucket_unpack_scale";
+  int st = check_copy(fn, plan, b, grad_arenas, bucket_bufs, N);
+  if (st != DDP_OK) return st;
+  const Bucket& bk = plan->buckets[b];
+  if (bk.n_tiles == 0) return DDP_OK;
+  const Segment* segs = nullptr;
+  st = device_segments(const_cast<ddp_plan*>(plan), &segs);
+  if (st != DDP_OK) return st;
+  RankPtrs A{}, B{};
+  for (int r = 0; r < N; ++r) {
+    A.p[r] = grad_arenas[r];
+    B.p[r] = const_cast<void*>(bucket_bufs[r]);
+  }
+  const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
+  hipStream_t s = as_stream(stream);
+  if (plan->dtype == DDP_FP32)
+    hipLaunchKernelGGL(k_unpack_scale<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs),
+                       bk.n_tiles, B, A, scale);
+  else
+    hipLaunchKernelGGL(k_unpack_scale<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs),
+                       bk.n_tiles, B, A, scale);
+  DDP_HIP_TRY(hipGetLastError(), "bucket_unpack_scale: launch");
+  return DDP_OK;
+}
+
+extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs,
+                        int32_t N, int32_t variant, float scale, void* stream) {
+  const char* fn = "ddp_sync";
+  if (plan == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": plan is NULL");
+  if (grad_arenas == nullptr || bucket_bufs == nullptr)
+    return fail(DDP_EINVAL, std::string(fn) + ": pointer array is NULL");
+  if (variant != DDP_VARIANT_FUSED && variant != DDP_VARIANT_STEPS && variant != DDP_VARIANT_PERSISTENT)
+    return fail(DDP_EINVAL, std::string(fn) + ": unknown variant");
+  if (N != plan->world_size) return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
+  for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
+    void* const* bufs = bucket_bufs + size_t(b) * N;
+    const int64_t count = plan->buckets[b].padded_numel;
+    int st = bucket_pack(plan, b, const_cast<const void* const*>(grad_arenas), bufs, N, stream);
+    if (st != DDP_OK) return st;
+    if (variant == DDP_VARIANT_FUSED) {
+      st = ring_allreduce_fused(bufs, N, count, plan->dtype, stream);
+    } else if (variant == DDP_VARIANT_PERSISTENT) {
+      st = ring_allreduce_persistent(bufs, N, count, plan->dtype, 2 * (N - 1), stream);
+    } else {
+      for (int ph = DDP_RS; ph <= DDP_AG && st == DDP_OK; ++ph)
+        for (int s = 0; s + 1 < N && st == DDP_OK; ++s)
+          st = ring_allreduce_step(bufs, N, count, plan->dtype, s, ph, stream);
+    }
+    if (st != DDP_OK) return st;
+    st = bucket_unpack_scale(plan, b, const_cast<const void* const*>(bufs), grad_arenas, N, scale, stream);
+    if (st != DDP_OK) return st;
+  }
+  return DDP_OK;
+}

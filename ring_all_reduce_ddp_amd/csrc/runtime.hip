@@ -1,0 +1,265 @@
+// Host-side argument checks, per-device barrier words, and the two helper
+// kernels (all-ranks-equal count, copy probe).
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "hip_common.h"
+
+namespace ddp {
+
+int check_range(const void* p, int64_t bytes, const char* fn, const char* what) {
+  if (bytes == 0) return DDP_OK;
+  if (p == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + what + " is NULL");
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  hipError_t e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DDP_EINVAL, std::string(fn) + ": " + what +
+                                " is not inside a device allocation of this process");
+  }
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+  const uintptr_t q = reinterpret_cast<uintptr_t>(p);
+  if (q < lo || uint64_t(bytes) > size || q - lo > size - uint64_t(bytes))
+    return fail(DDP_EINVAL, std::string(fn) + ": " + what + " range of " + std::to_string(bytes) +
+                                " bytes runs past the end of its allocation");
+  return DDP_OK;
+}
+
+int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, const char* fn,
+                       const char* what) {
+  if (bufs == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + what + " array is NULL");
+  std::vector<std::pair<uintptr_t, int32_t>> spans;
+  spans.reserve(n);
+  for (int32_t r = 0; r < n; ++r) {
+    const std::string name = std::string(what) + "[" + std::to_string(r) + "]";
+    if (bufs[r] == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is NULL");
+    if (reinterpret_cast<uintptr_t>(bufs[r]) % uintptr_t(align) != 0)
+      return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is not " + std::to_string(align) +
+                                  "-byte aligned");
+  }
+  for (int32_t r = 0; r < n; ++r) {
+    const std::string name = std::string(what) + "[" + std::to_string(r) + "]";
+    int st = check_range(bufs[r], bytes, fn, name.c_str());
+    if (st != DDP_OK) return st;
+    spans.emplace_back(reinterpret_cast<uintptr_t>(bufs[r]), r);
+  }
+  if (bytes > 0) {
+    std::sort(spans.begin(), spans.end());
+    for (size_t i = 1; i < spans.size(); ++i) {
+      if (spans[i].first - spans[i - 1].first < uint64_t(bytes))
+        return fail(DDP_EINVAL, std::string(fn) + ": " + what + "[" +
+                                    std::to_string(spans[i - 1].second) + "] and " + what + "[" +
+                                    std::to_string(spans[i].second) + "] overlap");
+    }
+  }
+  return DDP_OK;
+}
+
+bool all_aligned16(void* const* bufs, int32_t n) {
+  for (int32_t r = 0; r < n; ++r)
+    if (reinterpret_cast<uintptr_t>(bufs[r]) % 16 != 0) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------- barrier words
+
+namespace {
+
+constexpr int kSlots = 64;          // launches that may be in flight at once per device
+constexpr int kSlotStride = 64;     // words between slots (256 bytes)
+constexpr int kScratchWords = kSlots * kSlotStride + kSlotStride;  // + status line
+
+struct DeviceScratch {
+  unsigned int* words = nullptr;    // kScratchWords words; the last line holds the status
+  std::atomic<unsigned int> next{0};
+};
+
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+__global__ void k_zero_words(unsigned int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+int device_scratch(DeviceScratch** out) {
+  int dev = 0;
+  DDP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "device index beyond 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  DeviceScratch& s = g_scratch[dev];
+  if (s.words == nullptr) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, sizeof(unsigned int) * kScratchWords);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DDP_ENOMEM, std::string("barrier words: hipMalloc: ") + hipGetErrorString(e));
+    }
+    e = hipMemset(p, 0, sizeof(unsigned int) * kScratchWords);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "barrier words: hipMemset");
+    }
+    s.words = static_cast<unsigned int*>(p);
+  }
+  *out = &s;
+  return DDP_OK;
+}
+
+}  // namespace
+
+int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status) {
+  DeviceScratch* s = nullptr;
+  int st = device_scratch(&s);
+  if (st != DDP_OK) return st;
+  const unsigned int k = s->next.fetch_add(1u) % kSlots;
+  unsigned int* p = s->words + size_t(k) * kSlotStride;
+  // A fill kernel rather than a memset node keeps this usable under graph capture.
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, stream, p, kSlotStride);
+  DDP_HIP_TRY(hipGetLastError(), "barrier words: zero launch");
+  *slot = p;
+  *status = s->words + size_t(kSlots) * kSlotStride;
+  return DDP_OK;
+}
+
+// ---------------------------------------------------------------- all-ranks-equal count
+
+namespace {
+
+template <int EB>
+__global__ __launch_bounds__(kThreads) void k_count_mismatch(RankPtrs P, int n, int64_t count,
+                                                             unsigned long long* out) {
+  // EB: element bytes (2 or 4). Compares every rank's bits with rank 0's.
+  unsigned long long local = 0;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < count; i += stride) {
+    uint32_t ref, x;
+    if constexpr (EB == 4) {
+      ref = static_cast<const uint32_t*>(P.p[0])[i];
+    } else {
+      ref = static_cast<const uint16_t*>(P.p[0])[i];
+    }
+    bool diff = false;
+    for (int r = 1; r < n; ++r) {
+      if constexpr (EB == 4) {
+        x = static_cast<const uint32_t*>(P.p[r])[i];
+      } else {
+        x = static_cast<const uint16_t*>(P.p[r])[i];
+      }
+      diff |= (x != ref);
+    }
+    local += diff ? 1ull : 0ull;
+  }
+  __shared__ unsigned long long partial[kThreads];
+  partial[threadIdx.x] = local;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) partial[threadIdx.x] += partial[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && partial[0] != 0) atomicAdd(out, partial[0]);
+}
+
+__global__ void k_zero_u64(unsigned long long* p) {
+  if (threadIdx.x == 0) *p = 0ull;
+}
+
+// ---------------------------------------------------------------- copy probe
+
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void k_copy16(u32x4* __restrict__ dst,
+                                                     const u32x4* __restrict__ src, int64_t nvec) {
+  const int64_t tile = int64_t(kThreads) * kCopyUnroll;
+  for (int64_t base = int64_t(blockIdx.x) * tile; base < nvec; base += int64_t(gridDim.x) * tile) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < nvec) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < nvec) dst[i] = v[u];
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace ddp
+
+using namespace ddp;
+
+extern "C" int ddp_persistent_status(void* stream) {
+  DeviceScratch* s = nullptr;
+  int st = device_scratch(&s);
+  if (st != DDP_OK) return st;
+  DDP_HIP_TRY(hipStreamSynchronize(as_stream(stream)), "ddp_persistent_status: hipStreamSynchronize");
+  unsigned int* status = s->words + size_t(kSlots) * kSlotStride;
+  unsigned int host = 0;
+  DDP_HIP_TRY(hipMemcpy(&host, status, sizeof(host), hipMemcpyDeviceToHost),
+              "ddp_persistent_status: hipMemcpy");
+  if (host != 0) {
+    const unsigned int zero = 0;
+    DDP_HIP_TRY(hipMemcpy(status, &zero, sizeof(zero), hipMemcpyHostToDevice),
+                "ddp_persistent_status: hipMemcpy");
+    return fail(DDP_ETIMEOUT, "ring_allreduce_persistent: a grid barrier timed out; results are incomplete");
+  }
+  return DDP_OK;
+}
+
+extern "C" int ddp_count_mismatches(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                                    uint64_t* out_dev, void* stream) {
+  const char* fn = "ddp_count_mismatches";
+  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, std::string(fn) + ": unknown dtype");
+  if (N < 1 || N > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
+  if (count < 0) return fail(DDP_EINVAL, std::string(fn) + ": count < 0");
+  const int eb = elem_bytes(dtype);
+  int st = check_rank_buffers(bufs, N, count * eb, eb, fn, "bufs");
+  if (st != DDP_OK) return st;
+  st = check_range(out_dev, sizeof(uint64_t), fn, "out_dev");
+  if (st != DDP_OK) return st;
+  if (reinterpret_cast<uintptr_t>(out_dev) % 8 != 0)
+    return fail(DDP_EINVAL, std::string(fn) + ": out_dev is not 8-byte aligned");
+  hipStream_t s = as_stream(stream);
+  auto* out = reinterpret_cast<unsigned long long*>(out_dev);
+  hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, out);
+  DDP_HIP_TRY(hipGetLastError(), "ddp_count_mismatches: zero launch");
+  if (count == 0 || N == 1) return DDP_OK;
+  RankPtrs P{};
+  for (int r = 0; r < N; ++r) P.p[r] = bufs[r];
+  const int64_t blocks = std::min<int64_t>((count + kThreads - 1) / kThreads, 8192);
+  if (eb == 4)
+    hipLaunchKernelGGL(k_count_mismatch<4>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, P, N, count, out);
+  else
+    hipLaunchKernelGGL(k_count_mismatch<2>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, P, N, count, out);
+  DDP_HIP_TRY(hipGetLastError(), "ddp_count_mismatches: launch");
+  return DDP_OK;
+}
+
+extern "C" int ddp_copy_probe(void* dst, const void* src, int64_t nbytes, void* stream) {
+  const char* fn = "ddp_copy_probe";
+  if (nbytes < 0 || nbytes % 16 != 0)
+    return fail(DDP_EINVAL, std::string(fn) + ": nbytes must be a non-negative multiple of 16");
+  if (nbytes == 0) return DDP_OK;
+  if (reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(DDP_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+  int st = check_range(dst, nbytes, fn, "dst");
+  if (st != DDP_OK) return st;
+  st = check_range(src, nbytes, fn, "src");
+  if (st != DDP_OK) return st;
+  const uintptr_t d = reinterpret_cast<uintptr_t>(dst), q = reinterpret_cast<uintptr_t>(src);
+  if ((d < q ? q - d : d - q) < uint64_t(nbytes))
+    return fail(DDP_EINVAL, std::string(fn) + ": src and dst overlap");
+  const int64_t nvec = nbytes / 16;
+  const int64_t tile = int64_t(kThreads) * kCopyUnroll;
+  const int64_t blocks = std::min<int64_t>((nvec + tile - 1) / tile, int64_t(1) << 20);
+  hipLaunchKernelGGL(k_copy16, dim3(unsigned(blocks)), dim3(kThreads), 0, as_stream(stream),
+                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), nvec);
+  DDP_HIP_TRY(hipGetLastError(), "ddp_copy_probe: launch");
+  return DDP_OK;
+}

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, its host planner agrees with the oracle's, and bad arguments are
+refused before anything is launched (no GPU is touched by these calls)."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+rar = pytest.importorskip("ring_all_reduce_ddp_amd")
+
+from oracle import planner  # noqa: E402
+from ddp_workloads import resnet50_param_numels  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "ddp_ring.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["ddp_bucket_plan", "bucket_pack", "ring_allreduce_step", "ring_allreduce_fused",
+                 "ring_allreduce_persistent", "bucket_unpack_scale", "ddp_last_error", "ddp_sync"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rar.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert missing == []
+
+
+def test_only_one_hip_runtime_is_mapped():
+    maps = open("/proc/self/maps").read()
+    paths = set(re.findall(r"\S*libamdhip64\S*", maps))
+    assert len(paths) == 1, paths
+
+
+def as_tuples(buckets):
+    return [{"members": [tuple(m) for m in b["members"]], "padded_numel": b["padded_numel"]}
+            for b in buckets]
+
+
+def test_planner_matches_oracle_on_golden_cases(golden_dir):
+    with open(os.path.join(golden_dir, "planner_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        p = rar.ddp_bucket_plan(c["numels"], "fp32" if c["elem_bytes"] == 4 else "bf16",
+                                c["cap_bytes"], c["first_bucket_bytes"], c["world_size"])
+        assert p.buckets() == as_tuples(c["buckets"]), c["name"]
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_planner_matches_oracle_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    numels = [int(x) for x in rng.integers(0, 20000, size=rng.integers(0, 80))]
+    dt = ["fp32", "bf16"][seed % 2]
+    cap = int(rng.integers(16, 100000))
+    first = int(rng.integers(16, 100000))
+    n = int(rng.integers(1, 65))
+    p = rar.ddp_bucket_plan(numels, dt, cap, first, n)
+    want = planner.plan(numels, 4 if dt == "fp32" else 2, cap, first, n)
+    assert p.buckets() == as_tuples(want)
+
+
+def test_planner_resnet50_and_arena():
+    numels = resnet50_param_numels()
+    p = rar.ddp_bucket_plan(numels, "fp32", world_size=8)
+    assert p.buckets() == as_tuples(planner.plan(numels, 4, world_size=8))
+    n, offs = p.grad_arena()
+    assert offs[0] == 0 and all(o % 4 == 0 for o in offs)
+    assert all(offs[i + 1] - offs[i] == -(-numels[i] // 4) * 4 for i in range(len(numels) - 1))
+    assert n == offs[-1] + numels[-1]
+
+
+def expect_status(status, code, fragment):
+    assert status == code
+    assert fragment in rar.lib.ddp_last_error().decode()
+
+
+def test_planner_argument_errors():
+    lib = rar.lib
+    out = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 2)(4, -1)
+    expect_status(lib.ddp_bucket_plan(arr, 2, 0, 1024, 1024, 1, ctypes.byref(out)), rar.DDP_EINVAL, "negative")
+    arr = (ctypes.c_int64 * 1)(4)
+    expect_status(lib.ddp_bucket_plan(arr, 1, 7, 1024, 1024, 1, ctypes.byref(out)), rar.DDP_EINVAL, "dtype")
+    expect_status(lib.ddp_bucket_plan(arr, 1, 0, 0, 1024, 1, ctypes.byref(out)), rar.DDP_EINVAL, "capacities")
+    expect_status(lib.ddp_bucket_plan(arr, 1, 0, 1024, 1024, 65, ctypes.byref(out)), rar.DDP_EINVAL, "world_size")
+    expect_status(lib.ddp_bucket_plan(arr, 1, 0, 1024, 1024, 1, None), rar.DDP_EINVAL, "out")
+    p = rar.ddp_bucket_plan([4, 8], "fp32")
+    expect_status(lib.ddp_plan_bucket(p.handle, 5, None, None), rar.DDP_EINVAL, "out of range")
+    expect_status(lib.ddp_plan_member(p.handle, 0, 9, None, None, None), rar.DDP_EINVAL, "out of range")
+
+
+def test_ring_argument_errors_before_launch():
+    lib = rar.lib
+    bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    expect_status(lib.ring_allreduce_fused(bufs, 0, 10, rar.DDP_FP32, None), rar.DDP_EINVAL, "N must")
+    expect_status(lib.ring_allreduce_fused(bufs, 65, 10, rar.DDP_FP32, None), rar.DDP_EINVAL, "N must")
+    expect_status(lib.ring_allreduce_fused(bufs, 2, 10, 9, None), rar.DDP_EINVAL, "dtype")
+    expect_status(lib.ring_allreduce_fused(bufs, 2, -1, rar.DDP_FP32, None), rar.DDP_EINVAL, "count")
+    expect_status(lib.ring_allreduce_fused(None, 2, 10, rar.DDP_FP32, None), rar.DDP_EINVAL, "NULL")
+    nulls = (ctypes.c_void_p * 2)(0x1000, None)
+    expect_status(lib.ring_allreduce_fused(nulls, 2, 10, rar.DDP_FP32, None), rar.DDP_EINVAL, "bufs[1] is NULL")
+    odd = (ctypes.c_void_p * 2)(0x1001, 0x2000)
+    expect_status(lib.ring_allreduce_fused(odd, 2, 10, rar.DDP_FP32, None), rar.DDP_EINVAL, "aligned")
+    expect_status(lib.ring_allreduce_step(bufs, 2, 10, rar.DDP_FP32, 1, rar.DDP_RS, None), rar.DDP_EINVAL, "step")
+    expect_status(lib.ring_allreduce_step(bufs, 2, 10, rar.DDP_FP32, -1, rar.DDP_AG, None), rar.DDP_EINVAL, "step")
+    expect_status(lib.ring_allreduce_step(bufs, 2, 10, rar.DDP_FP32, 0, 5, None), rar.DDP_EINVAL, "phase")
+    expect_status(lib.ring_allreduce_persistent(bufs, 2, 10, rar.DDP_FP32, 3, None), rar.DDP_EINVAL, "n_steps")
+    expect_status(lib.ddp_copy_probe(None, None, 15, None), rar.DDP_EINVAL, "multiple of 16")
+    p = rar.ddp_bucket_plan([4, 8], "fp32", world_size=2)
+    expect_status(lib.bucket_pack(p.handle, 0, bufs, bufs, 3, None), rar.DDP_EINVAL, "world size")
+    expect_status(lib.bucket_pack(p.handle, 4, bufs, bufs, 2, None), rar.DDP_EINVAL, "out of range")
+    expect_status(lib.ddp_sync(p.handle, bufs, bufs, 2, 9, 0.5, None), rar.DDP_EINVAL, "variant")
+    # zero-length work is accepted without touching the device
+    assert lib.ring_allreduce_fused(bufs, 2, 0, rar.DDP_FP32, None) == rar.DDP_OK

@@ -1,0 +1,145 @@
+"""GPU parity of the bucket pack / unpack-with-scale kernels and of the whole
+DDP sync (ResNet-50 gradients, N=8) against the CPU oracle, bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import ring_all_reduce_ddp_amd as rar
+from oracle import ddp, planner
+from ddp_workloads import WORKLOADS, host_grads, resnet50_param_numels
+
+from gpu_util import TORCH_DTYPE, to_host, assert_bit_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def make_arenas(plan, grads, dtype):
+    """One device arena per rank holding the rank's gradients at the plan's offsets."""
+    arena_numel, offs = plan.grad_arena()
+    arenas = []
+    for g in grads:
+        a = np.zeros(arena_numel, np.float32)
+        for p, x in enumerate(g):
+            a[offs[p]:offs[p] + len(x)] = x
+        t = torch.from_numpy(a).cuda()
+        arenas.append(t.to(TORCH_DTYPE[dtype]) if dtype == "bf16" else t)
+    return arenas, offs
+
+
+def read_grads(arenas, offs, numels, dtype):
+    out = []
+    for a in arenas:
+        h = to_host(a, dtype)
+        out.append([h[offs[p]:offs[p] + m] for p, m in enumerate(numels)])
+    return out
+
+
+def bucket_buffers(plan, n, dtype, fill=float("nan")):
+    bufs = []
+    for b in range(plan.num_buckets):
+        padded, _ = plan.bucket(b)
+        bufs.append([torch.full((padded,), fill, dtype=TORCH_DTYPE[dtype], device="cuda") for _ in range(n)])
+    return bufs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_pack_then_unpack_is_identity(dtype):
+    numels = [7, 16, 1, 40, 3, 300, 9, 0, 5000, 33]
+    n = 3
+    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=4096, first_bucket_bytes=64, world_size=n)
+    grads = host_grads(21, n, numels)
+    if dtype == "bf16":
+        from ddp_workloads.gen import to_bf16_bits
+        grads = [[to_bf16_bits(x) for x in g] for g in grads]
+        grads_f32 = [[(x.astype(np.uint32) << 16).view(np.float32) for x in g] for g in grads]
+    else:
+        grads_f32 = grads
+    arenas, offs = make_arenas(plan, grads_f32, dtype)
+    buckets = bucket_buffers(plan, n, dtype)
+    oplan = planner.plan(numels, 4 if dtype == "fp32" else 2, 4096, 64, n)
+    for b in range(plan.num_buckets):
+        rar.bucket_pack(plan, b, arenas, buckets[b])
+    torch.cuda.synchronize()
+    for b in range(plan.num_buckets):
+        for r in range(n):
+            assert_bit_equal(to_host(buckets[b][r], dtype), ddp.pack(grads[r], oplan[b], dtype), f"pack b{b} r{r}")
+    out = [torch.zeros_like(a) for a in arenas]
+    for b in range(plan.num_buckets):
+        rar.bucket_unpack_scale(plan, b, buckets[b], out, 1.0)
+    torch.cuda.synchronize()
+    back = read_grads(out, offs, numels, dtype)
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(back[r][p], grads[r][p], f"unpack r{r} p{p}")
+
+
+@pytest.mark.parametrize("scale", [0.125, 1.0 / 3.0])
+def test_unpack_scale_rounding(scale):
+    numels = [1000, 4097]
+    n = 2
+    plan = rar.ddp_bucket_plan(numels, "fp32", world_size=n)
+    grads = host_grads(22, n, numels, std=1.0)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, n, "fp32")
+    oplan = planner.plan(numels, 4, world_size=n)
+    out = [torch.zeros_like(a) for a in arenas]
+    for b in range(plan.num_buckets):
+        rar.bucket_pack(plan, b, arenas, buckets[b])
+        rar.bucket_unpack_scale(plan, b, buckets[b], out, scale)
+    torch.cuda.synchronize()
+    back = read_grads(out, offs, numels, "fp32")
+    for b, bk in enumerate(oplan):
+        for r in range(n):
+            want = ddp.unpack_scale(ddp.pack(grads[r], bk, "fp32"), bk, np.float32(scale), "fp32")
+            for p, w in want.items():
+                assert_bit_equal(back[r][p], w, f"scale {scale} r{r} p{p}")
+
+
+def oracle_sync(grads, numels, n, dtype="fp32"):
+    oplan = planner.plan(numels, 4, world_size=n)
+    return ddp.ddp_sync(grads, oplan, dtype)
+
+
+@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
+def test_small_sync_against_oracle(variant):
+    numels = [7, 16, 1, 40, 3, 300, 9, 0, 5000, 33, 12345, 2]
+    n = 4
+    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=8192, first_bucket_bytes=256, world_size=n)
+    grads = host_grads(23, n, numels)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, n, "fp32")
+    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, "fp32")
+    oplan = planner.plan(numels, 4, 8192, 256, n)
+    want = ddp.ddp_sync(grads, oplan, "fp32")
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{variant} r{r} p{p}")
+
+
+@pytest.fixture(scope="module")
+def resnet50_case():
+    w = WORKLOADS["ddp_resnet50"]
+    numels = resnet50_param_numels()
+    grads = host_grads(w.seed, w.n, numels, std=w.std)
+    want = oracle_sync(grads, numels, w.n)
+    return w, numels, grads, want
+
+
+@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
+def test_resnet50_sync(resnet50_case, variant):
+    """The full sync of ResNet-50 gradients over 8 ranks: reverse-order buckets
+    (1 MiB first, 25 MiB cap), pack, all-reduce, x1/8, unpack."""
+    w, numels, grads, want = resnet50_case
+    plan = rar.ddp_bucket_plan(numels, "fp32", world_size=w.n)
+    assert plan.num_buckets == 6
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, w.n, "fp32")
+    rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=0.125)
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, "fp32")
+    for r in range(w.n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{variant} rank {r} param {p}")

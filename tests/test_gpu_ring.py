@@ -1,0 +1,207 @@
+"""GPU parity of the three ring all-reduce forms against the CPU oracle, bit
+for bit, on small and ragged inputs (several tiles, short and empty chunks,
+unaligned buffers, both dtypes) and hop by hop on the 3-rank example."""
+
+import numpy as np
+import pytest
+import torch
+
+import ring_all_reduce_ddp_amd as rar
+from oracle import ring
+from ddp_workloads import WORKLOADS, host_ring_inputs
+
+from gpu_util import to_device, to_host, assert_bit_equal
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["fused", "steps", "persistent"]
+
+
+def run_variant(variant, bufs, n_steps=None):
+    if variant == "fused":
+        rar.ring_allreduce_fused(bufs)
+    elif variant == "steps":
+        n = len(bufs)
+        k = 2 * (n - 1) if n_steps is None else n_steps
+        for i in range(k):
+            phase, s = (rar.DDP_RS, i) if i < n - 1 else (rar.DDP_AG, i - (n - 1))
+            rar.ring_allreduce_step(bufs, s, phase)
+    elif variant == "persistent":
+        rar.ring_allreduce_persistent(bufs, n_steps)
+    else:
+        raise ValueError(variant)
+    torch.cuda.synchronize()
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+
+
+def check_against_oracle(n, count, dtype, variant, seed, std=1e-3, pad_front=0, n_steps=None):
+    host = host_ring_inputs(seed, n, count, dtype, std=std)
+    want = ring.ring_simulate(host, dtype, n_steps=n_steps)["bufs"]
+    dev = to_device(host, dtype, pad_front=pad_front)
+    run_variant(variant, dev, n_steps)
+    for r in range(n):
+        assert_bit_equal(to_host(dev[r], dtype), want[r], f"{variant} n={n} count={count} {dtype} rank {r}")
+
+
+# ---------------------------------------------------------------- the 3-rank, 6-element example
+
+def c1_inputs():
+    w = WORKLOADS["ring_n3_6"]
+    return host_ring_inputs(w.seed, w.n, w.count, "fp32", dist=w.dist)
+
+
+@pytest.mark.parametrize("variant", ["steps", "persistent"])
+def test_c1_hop_by_hop(variant):
+    """State of every rank after each of the 4 steps equals the oracle's."""
+    host = c1_inputs()
+    states = ring.ring_simulate(host, "fp32", record=True)["states"]
+    for k in range(1, 5):
+        dev = to_device(host, "fp32")
+        run_variant(variant, dev, n_steps=k)
+        for r in range(3):
+            assert_bit_equal(to_host(dev[r], "fp32"), states[k - 1][2][r], f"{variant} after {k} steps, rank {r}")
+
+
+def test_c1_fused_and_exact_sum():
+    host = c1_inputs()
+    dev = to_device(host, "fp32")
+    run_variant("fused", dev)
+    want = np.sum(np.stack(host).astype(np.int64), axis=0)
+    for r in range(3):
+        assert np.array_equal(to_host(dev[r], "fp32").astype(np.int64), want)
+
+
+# ---------------------------------------------------------------- small and ragged
+
+SHAPES = [(2, 4096), (3, 6), (3, 7), (4, 3), (5, 12345), (7, 7 * 2048 * 3 + 11),
+          (8, 8 * 4096 * 2), (8, 8 * 4096 * 2 + 5), (8, 5), (9, 100_003), (16, 16 * 1000),
+          (33, 33 * 257 + 1), (64, 64 * 1024)]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n,count", SHAPES)
+def test_against_oracle(variant, dtype, n, count):
+    check_against_oracle(n, count, dtype, variant, seed=n * 1000 + count % 997)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_unaligned_buffers(variant, dtype):
+    """Buffers that start off a 16-byte boundary take the element-wise path."""
+    check_against_oracle(8, 8 * 3000, dtype, variant, seed=77, pad_front=1)
+
+
+@pytest.mark.parametrize("variant", ["steps", "persistent"])
+@pytest.mark.parametrize("k", [1, 3, 7, 8, 13])
+def test_partial_steps_n8(variant, k):
+    check_against_oracle(8, 8 * 5000 + 3, "fp32", variant, seed=k, n_steps=k)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_noops(variant):
+    """count = 0 and N = 1 leave the buffers untouched."""
+    one = to_device(host_ring_inputs(3, 1, 1000, "fp32"), "fp32")
+    before = to_host(one[0], "fp32")
+    if variant != "steps":  # a single rank has no steps to call
+        run_variant(variant, one)
+    assert_bit_equal(to_host(one[0], "fp32"), before, "N=1")
+    two = to_device(host_ring_inputs(3, 4, 10, "fp32"), "fp32")
+    snap = [to_host(t, "fp32") for t in two]
+    if variant == "fused":
+        rar.ring_allreduce_fused(two, count=0)
+    elif variant == "persistent":
+        rar.ring_allreduce_persistent(two, count=0)
+    else:
+        rar.ring_allreduce_step(two, 0, rar.DDP_RS, count=0)
+    torch.cuda.synchronize()
+    for t, s in zip(two, snap):
+        assert_bit_equal(to_host(t, "fp32"), s, "count=0")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_special_values(dtype):
+    """Subnormals are kept (no flush to zero), infinities propagate, signed
+    zeros follow IEEE; NaN positions (not payloads) agree."""
+    n, count = 4, 4096
+    rng = np.random.default_rng(5)
+    host = []
+    for r in range(n):
+        x = rng.normal(0, 1, count).astype(np.float32)
+        tiny = np.float32(2.0 ** -140) if dtype == "fp32" else np.float32(2.0 ** -128)
+        x[:1024] = (rng.integers(-3, 4, 1024) * tiny).astype(np.float32)   # subnormals
+        x[1024:1030] = [np.inf, -np.inf, 0.0, -0.0, 3e38, -3e38]
+        x[1030 + r] = np.nan
+        host.append(x)
+    if dtype == "bf16":
+        from ddp_workloads.gen import to_bf16_bits
+        host = [to_bf16_bits(x) for x in host]
+    want = ring.ring_simulate(host, dtype)["bufs"]
+    for variant in VARIANTS:
+        dev = to_device(host, dtype)
+        run_variant(variant, dev)
+        for r in range(n):
+            got = to_host(dev[r], dtype)
+            gv = got.view(np.uint32 if dtype == "fp32" else np.uint16)
+            wv = want[r].view(np.uint32 if dtype == "fp32" else np.uint16)
+            expo = 0x7F800000 if dtype == "fp32" else 0x7F80
+            frac = 0x007FFFFF if dtype == "fp32" else 0x007F
+            gnan = ((gv & expo) == expo) & ((gv & frac) != 0)
+            wnan = ((wv & expo) == expo) & ((wv & frac) != 0)
+            assert np.array_equal(gnan, wnan), (variant, r)
+            assert np.array_equal(gv[~wnan], wv[~wnan]), (variant, r)
+
+
+def hip_malloc(nbytes):
+    """A device allocation of exactly nbytes, straight from the HIP runtime
+    torch uses (torch's allocator rounds sizes up to its own segments)."""
+    import ctypes
+    import os
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    p = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(p), ctypes.c_size_t(nbytes)) == 0
+    return hip, p.value
+
+
+def test_errors_on_device_arguments():
+    """Ranges past an allocation and overlapping buffers are refused."""
+    import ctypes
+    hip, p = hip_malloc(4096)
+    try:
+        with pytest.raises(rar.DDPError, match="past the end"):
+            rar.ring_allreduce_fused([p, p + 2048], count=600, dtype="fp32")
+        rar.ring_allreduce_fused([p, p + 2048], count=512, dtype="fp32")   # exactly fits
+        torch.cuda.synchronize()
+    finally:
+        hip.hipFree(ctypes.c_void_p(p))
+    big = torch.zeros(1000, device="cuda")
+    with pytest.raises(rar.DDPError, match="overlap"):
+        rar.ring_allreduce_fused([big[:600], big[400:]], count=500)
+    with pytest.raises(rar.DDPError, match="not inside a device allocation"):
+        host = torch.zeros(100)
+        rar.ring_allreduce_fused([host, host.clone()], count=100, dtype="fp32")
+
+
+def test_mismatch_counter():
+    dev = to_device(host_ring_inputs(8, 4, 10000, "fp32"), "fp32")
+    out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rar.ddp_count_mismatches(dev, out)
+    torch.cuda.synchronize()
+    assert int(out.item()) > 9000
+    rar.ring_allreduce_fused(dev)
+    rar.ddp_count_mismatches(dev, out)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 0
+    dev[2][77] += 1.0
+    rar.ddp_count_mismatches(dev, out)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 1
+
+
+def test_copy_probe():
+    src = torch.randn(1 << 20, device="cuda")
+    dst = torch.empty_like(src)
+    rar.ddp_copy_probe(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
