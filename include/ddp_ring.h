@@ -165,14 +165,34 @@ int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dty
 /* The first n_steps of the 2(N-1) steps (RS steps first, then AG steps) in
  * one cooperative launch, with a grid-wide barrier between consecutive
  * steps. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce.
- * Returns DDP_ENORESOURCE if the grid cannot be co-resident. A barrier that
- * waits longer than its bound (seconds) lets every block exit and records a
- * sticky flag read by ddp_persistent_status. */
+ * Returns DDP_ENORESOURCE if the grid cannot be co-resident. A block that
+ * waits at a barrier longer than 10 s aborts the launch (every block exits,
+ * the result is incomplete) and sets a sticky flag read by
+ * ddp_persistent_status. */
 int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                               int32_t n_steps, void* stream);
 
+/* As ring_allreduce_persistent, with the launch's knobs exposed:
+ *   max_blocks: cooperative grid size (0: two blocks per compute unit, the
+ *       default); it is never more than one block per tile of a step, nor
+ *       more than one block per compute unit below the occupancy limit;
+ *   timeout_us: how long a block waits at a grid barrier before the launch
+ *       gives up (ring_allreduce_persistent uses 10 s); in (0, 3600 s];
+ *   extra_arrivals: added to every barrier's expected arrival count. It must
+ *       be 0 except in tests of the time-out path, where a non-zero value makes
+ *       every barrier wait for blocks that do not exist, so the launch times
+ *       out after timeout_us and every block exits. */
+int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                                 int32_t n_steps, int32_t max_blocks, int64_t timeout_us,
+                                 uint32_t extra_arrivals, void* stream);
+
+/* Cooperative grid size ring_allreduce_persistent would use for these
+ * arguments on the current device, and the device's compute-unit count. */
+int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int32_t* grid, int32_t* compute_units);
+
 /* Waits for `stream`, then reports DDP_ETIMEOUT if any persistent launch on
- * the current device timed out since the last call (and clears the flag). */
+ * the current device timed out since the last call (and clears the flag);
+ * the message gives the arrivals seen and expected at that barrier. */
 int ddp_persistent_status(void* stream);
 
 /* The whole all-reduce in one pass: every element is read once from each of

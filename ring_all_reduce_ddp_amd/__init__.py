@@ -66,6 +66,8 @@ def _load():
         "bucket_unpack_scale": (ctypes.c_int, [vp, i32, pp, pp, i32, f32, vp]),
         "ring_allreduce_step": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, vp]),
         "ring_allreduce_persistent": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
+        "ring_allreduce_persistent_ex": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, i64, ctypes.c_uint32, vp]),
+        "ddp_persistent_grid": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "ddp_persistent_status": (ctypes.c_int, [vp]),
         "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
         "ddp_sync": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, vp]),
@@ -235,6 +237,22 @@ def ring_allreduce_persistent(bufs, n_steps=None, count=None, dtype=None, stream
     if n_steps is None:
         n_steps = 2 * (n - 1)
     _check(lib.ring_allreduce_persistent(ptrs, n, count, dt, int(n_steps), _stream(stream)))
+
+
+def ring_allreduce_persistent_ex(bufs, n_steps=None, max_blocks=0, timeout_us=10_000_000,
+                                 extra_arrivals=0, count=None, dtype=None, stream=None):
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    if n_steps is None:
+        n_steps = 2 * (n - 1)
+    _check(lib.ring_allreduce_persistent_ex(ptrs, n, count, dt, int(n_steps), int(max_blocks),
+                                            int(timeout_us), int(extra_arrivals), _stream(stream)))
+
+
+def ddp_persistent_grid(n, count, dtype="fp32"):
+    """(grid, compute units) the persistent launch would use."""
+    g, cu = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.ddp_persistent_grid(int(n), int(count), dtype_code(dtype), ctypes.byref(g), ctypes.byref(cu)))
+    return g.value, cu.value
 
 
 def ddp_persistent_status(stream=None):

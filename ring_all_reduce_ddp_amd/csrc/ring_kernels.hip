@@ -40,7 +40,8 @@ constexpr int kFusedUnroll = 2;   // 16-byte vectors per thread per rank in the 
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
 constexpr int kBatch = 8;         // ranks loaded together by the any-N fused kernel
 constexpr int64_t kMaxGrid = int64_t(1) << 22;
-constexpr unsigned long long kSpinLimit = 1ull << 22;  // barrier polls before giving up
+constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
+constexpr int kPersistentBlocksPerCU = 2;  // default persistent grid: 512 blocks on 256 CUs
 
 __device__ __forceinline__ int wrap(int x, int n) {  // x in [0, 2n)
   return x >= n ? x - n : x;
@@ -231,48 +232,56 @@ __global__ __launch_bounds__(kThreads) void k_step(RankPtrs P, int n, int64_t co
 
 // ---------------------------------------------------------------- persistent
 
-// Grid-wide barrier for a cooperative launch. slot[0] counts arrivals over
-// the whole launch, slot[1] is the launch's abort flag; *status is the
-// device's sticky timeout flag. Returns false if the launch must stop.
-__device__ bool grid_barrier(unsigned int* slot, unsigned int target, unsigned int* status) {
+constexpr unsigned kAbortBit = 0x80000000u;
+
+// Grid-wide barrier for a cooperative launch. counter[0] counts arrivals over
+// the whole launch; its top bit is the launch's abort flag. A block that has
+// waited longer than `deadline` wall-clock ticks sets the abort bit, records
+// what it saw in status[0..2] (timed out, arrivals seen, arrivals expected),
+// and every block then leaves. Returns false if the launch must stop.
+__device__ bool grid_barrier(unsigned int* counter, unsigned int target, unsigned int* status,
+                             unsigned long long deadline) {
   __shared__ int ok;
   __syncthreads();  // every wave of the block has issued its stores of the step
   if (threadIdx.x == 0) {
     __threadfence();  // release at agent scope: the block's writes become visible to all XCDs
-    __hip_atomic_fetch_add(&slot[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int good = 1;
-    unsigned long long polls = 0;
-    while (__hip_atomic_load(&slot[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(&slot[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-        good = 0;
-        break;
+    unsigned int seen = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const unsigned long long t0 = wall_clock64();
+    while ((seen & kAbortBit) == 0u && seen < target) {
+      __builtin_amdgcn_s_sleep(4);
+      seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((seen & kAbortBit) == 0u && seen < target && wall_clock64() - t0 > deadline) {
+        const unsigned int prev =
+            __hip_atomic_fetch_or(counter, kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(&status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(&status[1], prev & ~kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(&status[2], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        seen = prev | kAbortBit;
       }
-      if (++polls > kSpinLimit) {
-        __hip_atomic_store(&slot[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        good = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
     }
     __threadfence();  // acquire at agent scope: the other blocks' writes are visible here
-    ok = good;
+    ok = (seen & kAbortBit) == 0u;
   }
   __syncthreads();
   return ok != 0;
 }
 
+// All n_steps steps, a grid barrier between consecutive ones. `extra` is
+// added to every barrier's expected arrival count; it is non-zero only when
+// a test forces the time-out path.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int64_t count, int64_t L,
                                                          int64_t tiles_per_chunk, int n_steps,
-                                                         unsigned int* slot, unsigned int* status) {
+                                                         unsigned int* counter, unsigned int* status,
+                                                         unsigned long long deadline, unsigned int extra) {
   const int64_t total_tiles = int64_t(n) * tiles_per_chunk;
   for (int i = 0; i < n_steps; ++i) {
     const int phase = i < n - 1 ? DDP_RS : DDP_AG;
     const int s = i < n - 1 ? i : i - (n - 1);
     for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
       step_tile<DT, VEC>(P, n, count, L, tiles_per_chunk, tile, s, phase);
-    if (i + 1 < n_steps && !grid_barrier(slot, unsigned(i + 1) * gridDim.x, status)) return;
+    if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
+      return;
   }
 }
 
@@ -367,29 +376,60 @@ int launch_step(const RingArgs& a, int step, int phase, hipStream_t s) {
   return a.vec ? launch_step_impl<DT, true>(a, step, phase, s) : launch_step_impl<DT, false>(a, step, phase, s);
 }
 
+struct PersistentOpts {
+  int32_t max_blocks = 0;       // 0: as many as can be co-resident
+  int64_t timeout_us = kDefaultTimeoutUs;
+  uint32_t extra_arrivals = 0;  // test hook: forces the time-out path
+};
+
+// Grid of the persistent kernel: kPersistentBlocksPerCU blocks per compute
+// unit (or max_blocks if > 0), never more than one block per tile of a step,
+// and never more than (occupancy - 1) blocks per compute unit. The headroom
+// is measured, not cosmetic: on MI355X the occupancy query reports 8 blocks
+// of this kernel per CU, yet a 2048-block cooperative grid had only 1792
+// blocks (7 per CU) running at the first barrier; the other 256 could not
+// start until those left, so the barrier could never complete.
 template <int DT, bool VEC>
-int launch_persistent_impl(const RingArgs& a, int n_steps, hipStream_t s) {
-  const int64_t tpc = step_tiles_per_chunk<DT>(a);
-  const int64_t total = tpc * a.n;
+int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* cus) {
+  const int64_t total = step_tiles_per_chunk<DT>(a) * a.n;
   const void* fn = reinterpret_cast<const void*>(&k_persistent<DT, VEC>);
-  int dev = 0, cus = 0, per_cu = 0;
+  int dev = 0, per_cu = 0;
   DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent: hipGetDevice");
-  DDP_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+  DDP_HIP_TRY(hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev),
               "ring_allreduce_persistent: multiprocessor count");
   DDP_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0),
               "ring_allreduce_persistent: occupancy");
-  const int64_t resident = int64_t(per_cu) * cus;
-  if (resident < 1) return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: no block can be resident");
-  const unsigned grid = unsigned(std::max<int64_t>(1, std::min(total, resident)));
+  if (per_cu < 1 || *cus < 1)
+    return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: no block can be resident");
+  const int64_t safe = int64_t(per_cu > 1 ? per_cu - 1 : 1) * (*cus);
+  const int64_t want = max_blocks > 0 ? int64_t(max_blocks) : int64_t(kPersistentBlocksPerCU) * (*cus);
+  *grid = unsigned(std::max<int64_t>(1, std::min({total, want, safe})));
+  return DDP_OK;
+}
+
+template <int DT, bool VEC>
+int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts& o, hipStream_t s) {
+  const int64_t tpc = step_tiles_per_chunk<DT>(a);
+  const void* fn = reinterpret_cast<const void*>(&k_persistent<DT, VEC>);
+  int dev = 0, clock_khz = 0, cus = 0;
+  unsigned grid = 0;
+  int st = persistent_grid<DT, VEC>(a, o.max_blocks, &grid, &cus);
+  if (st != DDP_OK) return st;
+  DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent: hipGetDevice");
+  DDP_HIP_TRY(hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev),
+              "ring_allreduce_persistent: wall clock rate");
   unsigned int* slot = nullptr;
   unsigned int* status = nullptr;
-  int st = barrier_slot(s, &slot, &status);
+  st = barrier_slot(s, &slot, &status);
   if (st != DDP_OK) return st;
   RankPtrs P = a.P;
   int n = a.n;
   int64_t count = a.count, L = a.L, tiles = tpc;
   int steps = n_steps;
-  void* args[] = {&P, &n, &count, &L, &tiles, &steps, &slot, &status};
+  unsigned long long deadline =
+      (unsigned long long)(std::max<int64_t>(clock_khz, 1)) * (unsigned long long)(o.timeout_us) / 1000ull;
+  unsigned int extra = o.extra_arrivals;
+  void* args[] = {&P, &n, &count, &L, &tiles, &steps, &slot, &status, &deadline, &extra};
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
   if (e == hipErrorCooperativeLaunchTooLarge) {
     (void)hipGetLastError();
@@ -397,6 +437,25 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, hipStream_t s) {
   }
   if (e != hipSuccess) return hip_fail(e, "ring_allreduce_persistent: hipLaunchCooperativeKernel");
   return DDP_OK;
+}
+
+int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int32_t dtype, int32_t n_steps,
+               const PersistentOpts& o, void* stream) {
+  if (N >= 1 && N <= DDP_MAX_RANKS && (n_steps < 0 || n_steps > 2 * (N - 1)))
+    return fail(DDP_EINVAL, std::string(fn) + ": n_steps must lie in [0, 2(N-1)]");
+  if (o.max_blocks < 0) return fail(DDP_EINVAL, std::string(fn) + ": max_blocks < 0");
+  if (o.timeout_us <= 0 || o.timeout_us > int64_t(3600) * 1000000)
+    return fail(DDP_EINVAL, std::string(fn) + ": timeout_us must lie in (0, 3600 s]");
+  RingArgs a;
+  int st = prepare(fn, bufs, N, count, dtype, &a);
+  if (st != DDP_OK) return st;
+  if (count == 0 || n_steps == 0) return DDP_OK;
+  hipStream_t s = as_stream(stream);
+  if (dtype == DDP_FP32)
+    return a.vec ? launch_persistent_impl<DDP_FP32, true>(a, n_steps, o, s)
+                 : launch_persistent_impl<DDP_FP32, false>(a, n_steps, o, s);
+  return a.vec ? launch_persistent_impl<DDP_BF16, true>(a, n_steps, o, s)
+               : launch_persistent_impl<DDP_BF16, false>(a, n_steps, o, s);
 }
 
 }  // namespace
@@ -430,17 +489,39 @@ extern "C" int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, 
 
 extern "C" int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                          int32_t n_steps, void* stream) {
-  const char* fn = "ring_allreduce_persistent";
-  if (N >= 1 && N <= DDP_MAX_RANKS && (n_steps < 0 || n_steps > 2 * (N - 1)))
-    return fail(DDP_EINVAL, std::string(fn) + ": n_steps must lie in [0, 2(N-1)]");
+  return persistent("ring_allreduce_persistent", bufs, N, count, dtype, n_steps, PersistentOpts{}, stream);
+}
+
+extern "C" int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int32_t* grid,
+                                   int32_t* compute_units) {
+  const char* fn = "ddp_persistent_grid";
+  if (grid == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": grid is NULL");
+  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, std::string(fn) + ": unknown dtype");
+  if (N < 1 || N > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
+  if (count < 1) return fail(DDP_EINVAL, std::string(fn) + ": count < 1");
   RingArgs a;
-  int st = prepare(fn, bufs, N, count, dtype, &a);
+  a.n = N;
+  a.count = count;
+  a.L = (count + N - 1) / N;
+  a.vec = a.L % (kVectorBytes / elem_bytes(dtype)) == 0;  // assuming 16-byte aligned buffers
+  unsigned g = 0;
+  int cus = 0;
+  int st = dtype == DDP_FP32 ? (a.vec ? persistent_grid<DDP_FP32, true>(a, 0, &g, &cus)
+                                      : persistent_grid<DDP_FP32, false>(a, 0, &g, &cus))
+                             : (a.vec ? persistent_grid<DDP_BF16, true>(a, 0, &g, &cus)
+                                      : persistent_grid<DDP_BF16, false>(a, 0, &g, &cus));
   if (st != DDP_OK) return st;
-  if (count == 0 || n_steps == 0) return DDP_OK;
-  hipStream_t s = as_stream(stream);
-  if (dtype == DDP_FP32)
-    return a.vec ? launch_persistent_impl<DDP_FP32, true>(a, n_steps, s)
-                 : launch_persistent_impl<DDP_FP32, false>(a, n_steps, s);
-  return a.vec ? launch_persistent_impl<DDP_BF16, true>(a, n_steps, s)
-               : launch_persistent_impl<DDP_BF16, false>(a, n_steps, s);
+  *grid = int32_t(g);
+  if (compute_units) *compute_units = cus;
+  return DDP_OK;
+}
+
+extern "C" int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                                            int32_t n_steps, int32_t max_blocks, int64_t timeout_us,
+                                            uint32_t extra_arrivals, void* stream) {
+  PersistentOpts o;
+  o.max_blocks = max_blocks;
+  o.timeout_us = timeout_us;
+  o.extra_arrivals = extra_arrivals;
+  return persistent("ring_allreduce_persistent_ex", bufs, N, count, dtype, n_steps, o, stream);
 }

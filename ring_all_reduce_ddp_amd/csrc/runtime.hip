@@ -200,14 +200,16 @@ extern "C" int ddp_persistent_status(void* stream) {
   if (st != DDP_OK) return st;
   DDP_HIP_TRY(hipStreamSynchronize(as_stream(stream)), "ddp_persistent_status: hipStreamSynchronize");
   unsigned int* status = s->words + size_t(kSlots) * kSlotStride;
-  unsigned int host = 0;
-  DDP_HIP_TRY(hipMemcpy(&host, status, sizeof(host), hipMemcpyDeviceToHost),
+  unsigned int host[3] = {0, 0, 0};
+  DDP_HIP_TRY(hipMemcpy(host, status, sizeof(host), hipMemcpyDeviceToHost),
               "ddp_persistent_status: hipMemcpy");
-  if (host != 0) {
-    const unsigned int zero = 0;
-    DDP_HIP_TRY(hipMemcpy(status, &zero, sizeof(zero), hipMemcpyHostToDevice),
+  if (host[0] != 0) {
+    const unsigned int zero[3] = {0, 0, 0};
+    DDP_HIP_TRY(hipMemcpy(status, zero, sizeof(zero), hipMemcpyHostToDevice),
                 "ddp_persistent_status: hipMemcpy");
-    return fail(DDP_ETIMEOUT, "ring_allreduce_persistent: a grid barrier timed out; results are incomplete");
+    return fail(DDP_ETIMEOUT, "ring_allreduce_persistent: a grid barrier timed out with " +
+                                  std::to_string(host[1]) + " of " + std::to_string(host[2]) +
+                                  " block arrivals; results are incomplete");
   }
   return DDP_OK;
 }

@@ -205,3 +205,41 @@ def test_copy_probe():
     rar.ddp_copy_probe(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def test_persistent_grid_leaves_headroom():
+    grid, cus = rar.ddp_persistent_grid(8, 268435456, "fp32")
+    assert 1 <= grid <= 2 * cus
+    small, _ = rar.ddp_persistent_grid(3, 6, "fp32")
+    assert small == 3   # one block per tile of a step
+
+
+def test_persistent_timeout_path_exits_and_reports():
+    """A barrier told to wait for one block more than the grid has gives up
+    after its deadline (20 ms here): every block exits, the status call
+    reports the time-out once, and the next launch is unaffected."""
+    host = host_ring_inputs(31, 4, 4 * 8192, "fp32")
+    dev = to_device(host, "fp32")
+    rar.ring_allreduce_persistent_ex(dev, extra_arrivals=1, timeout_us=20_000)
+    torch.cuda.synchronize()
+    with pytest.raises(rar.DDPError, match="timed out"):
+        rar.ddp_persistent_status()
+    rar.ddp_persistent_status()          # the flag was cleared
+    dev = to_device(host, "fp32")
+    run_variant("persistent", dev)
+    want = ring.ring_simulate(host, "fp32")["bufs"]
+    for r in range(4):
+        assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"after a time-out, rank {r}")
+
+
+@pytest.mark.parametrize("max_blocks", [1, 7, 256, 1000])
+def test_persistent_grid_sizes(max_blocks):
+    """Any cooperative grid size gives the same bits."""
+    host = host_ring_inputs(32, 8, 8 * 40000 + 8, "fp32")
+    want = ring.ring_simulate(host, "fp32")["bufs"]
+    dev = to_device(host, "fp32")
+    rar.ring_allreduce_persistent_ex(dev, max_blocks=max_blocks)
+    torch.cuda.synchronize()
+    rar.ddp_persistent_status()
+    for r in range(8):
+        assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"max_blocks={max_blocks} rank {r}")
