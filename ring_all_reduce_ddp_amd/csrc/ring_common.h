@@ -1,0 +1,46 @@
+// Argument checking and launch helpers shared by the ring kernels
+// (ring_kernels.hip: step and persistent forms; fused_kernels.hip: fused form).
+#pragma once
+
+#include <algorithm>
+
+#include "hip_common.h"
+
+namespace ddp {
+
+constexpr int64_t kMaxGrid = int64_t(1) << 22;
+
+__device__ __forceinline__ int wrap(int x, int n) {  // x in [0, 2n)
+  return x >= n ? x - n : x;
+}
+
+struct RingArgs {
+  RankPtrs P{};
+  int n = 0;
+  int64_t count = 0;
+  int64_t L = 0;
+  bool vec = false;
+};
+
+inline int prepare(const char* fn, void* const* bufs, int32_t N, int64_t count, int32_t dtype, RingArgs* a) {
+  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, std::string(fn) + ": unknown dtype");
+  if (N < 1 || N > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
+  if (count < 0) return fail(DDP_EINVAL, std::string(fn) + ": count < 0");
+  const int eb = elem_bytes(dtype);
+  if (count > (int64_t(1) << 40)) return fail(DDP_EINVAL, std::string(fn) + ": count too large");
+  int st = check_rank_buffers(bufs, N, count * eb, eb, fn, "bufs");
+  if (st != DDP_OK) return st;
+  a->n = N;
+  a->count = count;
+  a->L = (count + N - 1) / N;
+  const int V = kVectorBytes / eb;
+  a->vec = (a->L % V == 0) && all_aligned16(bufs, N);
+  for (int r = 0; r < N; ++r) a->P.p[r] = bufs[r];
+  return DDP_OK;
+}
+
+inline unsigned grid_for(int64_t total_tiles) {
+  return unsigned(std::max<int64_t>(1, std::min(total_tiles, kMaxGrid)));
+}
+
+}  // namespace ddp

@@ -1,4 +1,4 @@
-// Ring all-reduce over N virtual ranks held in one GPU's HBM.
+// Step-faithful ring all-reduce over N virtual ranks held in one GPU's HBM.
 //
 // Method (page "DDP 与 Ring All-Reduce", blog.vllbc.top, section 03; page "DDP 与
 // Ring-AllReduce", xuesongtap.github.io, §1.3.1 and the worked example of
@@ -9,7 +9,7 @@
 // thus starts at rank c+1, collects ranks c+2, ..., c, one rounded add per
 // hop, and ends complete on rank c, from where it travels on unchanged.
 //
-// Three forms share that arithmetic:
+// Two forms run the steps as steps (the one-pass form is in fused_kernels.hip):
 //   * ring_allreduce_step: one launch per step, covering all N transfers of
 //     the step. Within a step the N transfers touch disjoint chunks (rank r
 //     writes chunk (r-1-s) of rank r+1 and reads chunk (r-1-s) of rank r, which
@@ -17,147 +17,22 @@
 //   * ring_allreduce_persistent: all steps in one cooperative launch, with a
 //     grid-wide barrier between steps (the per-step synchronisation of a real
 //     ring).
-//   * ring_allreduce_fused: each element is read once from every rank, summed
-//     in exactly the order the hops would add it, and written to every rank.
-//     Per element the steps only ever combine the N ranks' values at the same
-//     position, so this reproduces the final state of the 2(N-1) steps bit
-//     for bit, with 2*N*S bytes of HBM traffic instead of 5*(N-1)*S.
 //
-// All kernels stream 16-byte vectors when every chunk starts on a 16-byte
-// boundary (L a multiple of the elements per vector and 16-byte aligned
-// buffers), and fall back to one element per thread otherwise. A block works
-// on tiles that never cross a chunk boundary, so the rank order of a tile is
-// uniform across the block. No LDS and no matrix cores: nothing here is
+// Both stream 16-byte vectors when every chunk starts on a 16-byte boundary
+// (L a multiple of the elements per vector and 16-byte aligned buffers), and
+// fall back to one element per thread otherwise. A block works on tiles that
+// never cross a chunk boundary. No LDS and no matrix cores: nothing here is
 // reused across threads or shaped like a contraction.
 #include <algorithm>
 
-#include "hip_common.h"
+#include "ring_common.h"
 
 namespace ddp {
 namespace {
 
-constexpr int kFusedUnroll = 2;   // 16-byte vectors per thread per rank in the fused kernel
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
-constexpr int kBatch = 8;         // ranks loaded together by the any-N fused kernel
-constexpr int64_t kMaxGrid = int64_t(1) << 22;
 constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
 constexpr int kPersistentBlocksPerCU = 2;  // default persistent grid: 512 blocks on 256 CUs
-
-__device__ __forceinline__ int wrap(int x, int n) {  // x in [0, 2n)
-  return x >= n ? x - n : x;
-}
-
-// ---------------------------------------------------------------- fused, fixed N
-
-template <int DT, int NR, int U, bool NT>
-__global__ __launch_bounds__(kThreads) void k_fused_vec(RankPtrs P, int64_t count, int64_t L,
-                                                        int64_t tiles_per_chunk, int64_t total_tiles) {
-  using O = Ops<DT>;
-  constexpr int V = O::V;
-  constexpr int64_t kTile = int64_t(kThreads) * U * V;
-  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    const int c = int(tile / tiles_per_chunk);
-    const int64_t lo = int64_t(c) * L;
-    const int64_t hi = min(lo + L, count);
-    const int64_t base = lo + (tile - int64_t(c) * tiles_per_chunk) * kTile;
-    if (base >= hi) continue;
-    // Ring order of chunk c: rank c+1 first, then c+2, ..., c.
-    const void* src[NR];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) src[k] = P.p[wrap(c + 1 + k, NR)];
-    u32x4 x[U][NR];
-    int64_t vi[U];
-    bool full[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      vi[u] = base / V + int64_t(u) * kThreads + threadIdx.x;
-      full[u] = (vi[u] + 1) * V <= hi;
-      if (full[u]) {
-#pragma unroll
-        for (int k = 0; k < NR; ++k) x[u][k] = ld16<NT>(static_cast<const u32x4*>(src[k]) + vi[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (full[u]) {
-        typename O::Acc a = O::from(x[u][0]);
-#pragma unroll
-        for (int k = 1; k < NR; ++k) O::add(a, x[u][k]);
-        const u32x4 y = O::to(a);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) st16<NT>(static_cast<u32x4*>(P.p[r]) + vi[u], y);
-      } else {
-        // Ragged end of the buffer: the elements of this vector below `hi`.
-        const int64_t e0 = vi[u] * V;
-        for (int64_t e = e0; e < hi && e < e0 + V; ++e) {
-          float acc = O::load1(src[0], e);
-          for (int k = 1; k < NR; ++k) acc = O::add1(acc, O::load1(src[k], e));
-          for (int r = 0; r < NR; ++r) O::store1(P.p[r], e, acc);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- fused, any N
-
-template <int DT, bool NT>
-__global__ __launch_bounds__(kThreads) void k_fused_vec_n(RankPtrs P, int n, int64_t count, int64_t L,
-                                                          int64_t tiles_per_chunk, int64_t total_tiles) {
-  using O = Ops<DT>;
-  constexpr int V = O::V;
-  constexpr int64_t kTile = int64_t(kThreads) * V;
-  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    const int c = int(tile / tiles_per_chunk);
-    const int64_t lo = int64_t(c) * L;
-    const int64_t hi = min(lo + L, count);
-    const int64_t base = lo + (tile - int64_t(c) * tiles_per_chunk) * kTile;
-    if (base >= hi) continue;
-    const int64_t vi = base / V + threadIdx.x;
-    const int first = wrap(c + 1, n);
-    if ((vi + 1) * V <= hi) {
-      typename O::Acc a = O::from(ld16<NT>(static_cast<const u32x4*>(P.p[first]) + vi));
-      // Ranks c+2, ..., c in order, loaded kBatch at a time.
-      for (int k = 1; k < n; k += kBatch) {
-        u32x4 x[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          if (k + j < n) x[j] = ld16<NT>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-          if (k + j < n) O::add(a, x[j]);
-      }
-      const u32x4 y = O::to(a);
-      for (int r = 0; r < n; ++r) st16<NT>(static_cast<u32x4*>(P.p[r]) + vi, y);
-    } else {
-      const int64_t e0 = vi * V;
-      for (int64_t e = e0; e < hi && e < e0 + V; ++e) {
-        float acc = O::load1(P.p[first], e);
-        for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
-        for (int r = 0; r < n; ++r) O::store1(P.p[r], e, acc);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- fused, one element per thread
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_fused_scalar(RankPtrs P, int n, int64_t count, int64_t L,
-                                                           int64_t tiles_per_chunk, int64_t total_tiles) {
-  using O = Ops<DT>;
-  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    const int c = int(tile / tiles_per_chunk);
-    const int64_t lo = int64_t(c) * L;
-    const int64_t hi = min(lo + L, count);
-    const int64_t e = lo + (tile - int64_t(c) * tiles_per_chunk) * kThreads + threadIdx.x;
-    if (e >= hi) continue;
-    const int first = wrap(c + 1, n);
-    float acc = O::load1(P.p[first], e);
-    for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
-    for (int r = 0; r < n; ++r) O::store1(P.p[r], e, acc);
-  }
-}
 
 // ---------------------------------------------------------------- one step
 
@@ -287,71 +162,6 @@ __global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int6
 
 // ---------------------------------------------------------------- host side
 
-struct RingArgs {
-  RankPtrs P{};
-  int n = 0;
-  int64_t count = 0;
-  int64_t L = 0;
-  bool vec = false;
-};
-
-int prepare(const char* fn, void* const* bufs, int32_t N, int64_t count, int32_t dtype, RingArgs* a) {
-  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, std::string(fn) + ": unknown dtype");
-  if (N < 1 || N > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
-  if (count < 0) return fail(DDP_EINVAL, std::string(fn) + ": count < 0");
-  const int eb = elem_bytes(dtype);
-  if (count > (int64_t(1) << 40)) return fail(DDP_EINVAL, std::string(fn) + ": count too large");
-  int st = check_rank_buffers(bufs, N, count * eb, eb, fn, "bufs");
-  if (st != DDP_OK) return st;
-  a->n = N;
-  a->count = count;
-  a->L = (count + N - 1) / N;
-  const int V = kVectorBytes / eb;
-  a->vec = (a->L % V == 0) && all_aligned16(bufs, N);
-  for (int r = 0; r < N; ++r) a->P.p[r] = bufs[r];
-  return DDP_OK;
-}
-
-inline unsigned grid_for(int64_t total_tiles) {
-  return unsigned(std::max<int64_t>(1, std::min(total_tiles, kMaxGrid)));
-}
-
-template <int DT>
-int launch_fused(const RingArgs& a, hipStream_t s) {
-  constexpr int V = Ops<DT>::V;
-  if (a.vec) {
-    const bool fixed = a.n >= 2 && a.n <= 8;
-    const int64_t tile = int64_t(kThreads) * (fixed ? kFusedUnroll : 1) * V;
-    const int64_t tpc = (a.L + tile - 1) / tile;
-    const int64_t total = tpc * a.n;
-    const dim3 g(grid_for(total)), b(kThreads);
-    switch (a.n) {
-#define DDP_FUSED_CASE(NR)                                                                     \
-  case NR:                                                                                     \
-    hipLaunchKernelGGL((k_fused_vec<DT, NR, kFusedUnroll, false>), g, b, 0, s, a.P, a.count, \
-                       a.L, tpc, total);                                                       \
-    break;
-      DDP_FUSED_CASE(2)
-      DDP_FUSED_CASE(3)
-      DDP_FUSED_CASE(4)
-      DDP_FUSED_CASE(5)
-      DDP_FUSED_CASE(6)
-      DDP_FUSED_CASE(7)
-      DDP_FUSED_CASE(8)
-#undef DDP_FUSED_CASE
-      default:
-        hipLaunchKernelGGL((k_fused_vec_n<DT, false>), g, b, 0, s, a.P, a.n, a.count, a.L, tpc, total);
-    }
-  } else {
-    const int64_t tpc = (a.L + kThreads - 1) / kThreads;
-    const int64_t total = tpc * a.n;
-    hipLaunchKernelGGL((k_fused_scalar<DT>), dim3(grid_for(total)), dim3(kThreads), 0, s, a.P, a.n,
-                       a.count, a.L, tpc, total);
-  }
-  DDP_HIP_TRY(hipGetLastError(), "ring_allreduce_fused: launch");
-  return DDP_OK;
-}
-
 template <int DT>
 int64_t step_tiles_per_chunk(const RingArgs& a) {
   const int64_t tile = a.vec ? int64_t(kThreads) * kStepUnroll * Ops<DT>::V : kThreads;
@@ -462,16 +272,6 @@ int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int3
 }  // namespace ddp
 
 using namespace ddp;
-
-extern "C" int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
-                                    void* stream) {
-  RingArgs a;
-  int st = prepare("ring_allreduce_fused", bufs, N, count, dtype, &a);
-  if (st != DDP_OK) return st;
-  if (count == 0 || N == 1) return DDP_OK;  // one rank: the ring has no steps
-  return dtype == DDP_FP32 ? launch_fused<DDP_FP32>(a, as_stream(stream))
-                           : launch_fused<DDP_BF16>(a, as_stream(stream));
-}
 
 extern "C" int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                    int32_t step, int32_t phase, void* stream) {
