@@ -18,14 +18,18 @@ namespace {
 //
 // Launch shape, measured on MI355X at 8 ranks x 1 GiB: one wave (64 threads)
 // per block, one 16-byte vector per thread per rank, one tile per block, and
-// non-temporal loads and stores (the data is touched once). Single-wave
-// blocks retire independently, which kept the memory system busier than
-// 256-thread blocks (5.86 vs 5.50 TB/s for fp32); grid-stride loops over a
-// resident grid were slower still. Tiles are numbered either chunk-major
-// (tile t of chunk c is block c * tiles_per_chunk + t) or interleaved across
-// chunks (block t * N + c); fp32 ran faster interleaved and bf16 chunk-major.
+// non-temporal stores (the result is not read again by this kernel).
+// Single-wave blocks retire independently, which kept the memory system
+// busier than 256-thread blocks (5.86 vs 5.50 TB/s for fp32); grid-stride
+// loops over a resident grid were slower still. Loads are non-temporal when
+// the N buffers together exceed the 256 MB Infinity Cache; when they fit
+// (a DDP bucket: 8 x 25 MiB) cached loads find data written just before
+// (7.05 vs 6.65 TB/s). Tiles are numbered either chunk-major (tile t of
+// chunk c is block c * tiles_per_chunk + t) or interleaved across chunks
+// (block t * N + c); fp32 ran faster interleaved and bf16 chunk-major.
 
 constexpr int kFusedThreads = 64;
+constexpr int64_t kFusedCacheResidentBytes = int64_t(256) << 20;
 constexpr int kFusedBatch = 16;   // ranks loaded together by the any-N kernel
 
 template <int DT>
@@ -44,7 +48,7 @@ __device__ __forceinline__ void fused_tile(int64_t tile, int n, int64_t tiles_pe
   }
 }
 
-template <int DT, int NR>
+template <int DT, int NR, bool NTL>
 __global__ __launch_bounds__(kFusedThreads) void k_fused_vec(RankPtrs P, int64_t count, int64_t L,
                                                              int64_t tiles_per_chunk, int64_t total_tiles) {
   using O = Ops<DT>;
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused_vec(RankPtrs P, int64_t
     if ((vi + 1) * V <= hi) {
       u32x4 x[NR];
 #pragma unroll
-      for (int k = 0; k < NR; ++k) x[k] = ld16<true>(static_cast<const u32x4*>(src[k]) + vi);
+      for (int k = 0; k < NR; ++k) x[k] = ld16<NTL>(static_cast<const u32x4*>(src[k]) + vi);
       typename O::Acc a = O::from(x[0]);
 #pragma unroll
       for (int k = 1; k < NR; ++k) O::add(a, x[k]);
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused_vec(RankPtrs P, int64_t
   }
 }
 
-template <int DT>
+template <int DT, bool NTL>
 __global__ __launch_bounds__(kFusedThreads) void k_fused_vec_n(RankPtrs P, int n, int64_t count, int64_t L,
                                                                int64_t tiles_per_chunk, int64_t total_tiles) {
   using O = Ops<DT>;
@@ -97,13 +101,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused_vec_n(RankPtrs P, int n
     if (vi * V >= hi) continue;
     const int first = wrap(c + 1, n);
     if ((vi + 1) * V <= hi) {
-      typename O::Acc a = O::from(ld16<true>(static_cast<const u32x4*>(P.p[first]) + vi));
+      typename O::Acc a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
       // Ranks c+2, ..., c in order, loaded kFusedBatch at a time.
       for (int k = 1; k < n; k += kFusedBatch) {
         u32x4 x[kFusedBatch];
 #pragma unroll
         for (int j = 0; j < kFusedBatch; ++j)
-          if (k + j < n) x[j] = ld16<true>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
+          if (k + j < n) x[j] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
 #pragma unroll
         for (int j = 0; j < kFusedBatch; ++j)
           if (k + j < n) O::add(a, x[j]);
@@ -140,30 +144,38 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RankPtrs P, int n, in
   }
 }
 
+template <int DT, bool NTL>
+void launch_fused_vec(const RingArgs& a, hipStream_t s) {
+  constexpr int V = Ops<DT>::V;
+  const int64_t tile = int64_t(kFusedThreads) * V;
+  const int64_t tpc = (a.L + tile - 1) / tile;
+  const int64_t total = tpc * a.n;
+  const dim3 g(grid_for(total)), b(kFusedThreads);
+  switch (a.n) {
+#define DDP_FUSED_CASE(NR)                                                                      \
+  case NR:                                                                                      \
+    hipLaunchKernelGGL((k_fused_vec<DT, NR, NTL>), g, b, 0, s, a.P, a.count, a.L, tpc, total);  \
+    break;
+    DDP_FUSED_CASE(2)
+    DDP_FUSED_CASE(3)
+    DDP_FUSED_CASE(4)
+    DDP_FUSED_CASE(5)
+    DDP_FUSED_CASE(6)
+    DDP_FUSED_CASE(7)
+    DDP_FUSED_CASE(8)
+#undef DDP_FUSED_CASE
+    default:
+      hipLaunchKernelGGL((k_fused_vec_n<DT, NTL>), g, b, 0, s, a.P, a.n, a.count, a.L, tpc, total);
+  }
+}
+
 template <int DT>
 int launch_fused(const RingArgs& a, hipStream_t s) {
-  constexpr int V = Ops<DT>::V;
   if (a.vec) {
-    const int64_t tile = int64_t(kFusedThreads) * V;
-    const int64_t tpc = (a.L + tile - 1) / tile;
-    const int64_t total = tpc * a.n;
-    const dim3 g(grid_for(total)), b(kFusedThreads);
-    switch (a.n) {
-#define DDP_FUSED_CASE(NR)                                                                           \
-  case NR:                                                                                           \
-    hipLaunchKernelGGL((k_fused_vec<DT, NR>), g, b, 0, s, a.P, a.count, a.L, tpc, total);            \
-    break;
-      DDP_FUSED_CASE(2)
-      DDP_FUSED_CASE(3)
-      DDP_FUSED_CASE(4)
-      DDP_FUSED_CASE(5)
-      DDP_FUSED_CASE(6)
-      DDP_FUSED_CASE(7)
-      DDP_FUSED_CASE(8)
-#undef DDP_FUSED_CASE
-      default:
-        hipLaunchKernelGGL((k_fused_vec_n<DT>), g, b, 0, s, a.P, a.n, a.count, a.L, tpc, total);
-    }
+    if (int64_t(a.n) * a.count * elem_bytes(DT) > kFusedCacheResidentBytes)
+      launch_fused_vec<DT, true>(a, s);
+    else
+      launch_fused_vec<DT, false>(a, s);
   } else {
     const int64_t tpc = (a.L + kThreads - 1) / kThreads;
     const int64_t total = tpc * a.n;
