@@ -175,11 +175,16 @@ def main():
     sizes = [plan.bucket(b)[0] * 4 for b in range(plan.num_buckets)]
     grad_bytes = sum(numels) * 4
     sync = {"bucket_sizes": sizes, "params": len(numels), "grad_bytes_per_rank": grad_bytes}
-    for variant in ("fused", "steps", "persistent"):
-        rar.ddp_sync(plan, arenas, buckets, variant=variant)
-        t = time_launches(lambda: rar.ddp_sync(plan, arenas, buckets, variant=variant), reps, torch)
+    for variant in ("fused", "steps", "persistent", "view"):
+        bb = None if variant == "view" else buckets
+        rar.ddp_sync(plan, arenas, bb, variant=variant)
+        t = time_launches(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), reps, torch)
         sync[variant] = {"ms": round(t, 4),
                          "bus_gbps": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
+        if variant in ("fused", "view"):
+            # pack + fused + unpack move 6*N*S; the in-place sync 2*N*S (padding excluded)
+            sync_bytes = (2 if variant == "view" else 6) * wr.n * grad_bytes
+            sync[variant]["hbm_gbps_algorithmic"] = round(gbps(sync_bytes, t), 1)
     extras["ddp_sync_resnet50_n8"] = sync
     del arenas, buckets
     torch.cuda.empty_cache()

@@ -75,6 +75,7 @@ extern "C" {
 #define DDP_VARIANT_FUSED 0
 #define DDP_VARIANT_STEPS 1
 #define DDP_VARIANT_PERSISTENT 2
+#define DDP_VARIANT_VIEW 3       /* in place, no bucket buffers: bucket_allreduce_view */
 
 typedef struct ddp_plan ddp_plan; /* opaque; host memory owned by the library */
 
@@ -204,13 +205,33 @@ int ddp_persistent_status(void* stream);
 int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                          void* stream);
 
+/* bucket_allreduce_view: the all-reduce of bucket b done in place on the
+ * gradients, with no bucket buffer (the analogue of DDP's
+ * gradient_as_bucket_view=True, [R] sections 03 and 05; [D] "bucket 与
+ * overlap": the gradients are views of the bucket, so the gradient<->bucket
+ * copies and one gradient's worth of memory disappear). Every member element
+ * keeps its position in the bucket's layout, hence its ring chunk c and its
+ * summation order (rank c+1 first, then c+2, ..., c, one rounding per add);
+ * the sum is multiplied by `scale` (one rounding) and written to every rank's
+ * gradient. The result equals bucket_pack + ring_allreduce_fused +
+ * bucket_unpack_scale bit for bit, with 2*N*S_b bytes of traffic instead of
+ * 6*N*S_b.
+ *   grad_arenas[N]: device pointers, 16-byte aligned, each arena_numel elements
+ *       laid out by ddp_plan_grad_arena; read and overwritten (members only).
+ *   N must equal the plan's world size. */
+int bucket_allreduce_view(const ddp_plan* plan, int32_t b, void* const* grad_arenas, int32_t N,
+                          float scale, void* stream);
+
 /* ---------------------------------------------------------------- whole sync
  * ddp_sync: one DDP gradient synchronisation. For every bucket b in plan
- * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_*) on
- * bucket b's N buffers, bucket_unpack_scale with `scale` (pass 1/N for DDP's
- * mean). Bucket i+1 is never started before bucket i ([R] section 03).
+ * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_FUSED,
+ * _STEPS or _PERSISTENT) on bucket b's N buffers, bucket_unpack_scale with
+ * `scale` (pass 1/N for DDP's mean); or, for DDP_VARIANT_VIEW,
+ * bucket_allreduce_view on the gradients themselves. Bucket i+1 is never
+ * started before bucket i ([R] section 03).
  *   grad_arenas[N]: as for bucket_pack.
- *   bucket_bufs[B*N]: bucket b of rank r at index b*N + r (host array).
+ *   bucket_bufs[B*N]: bucket b of rank r at index b*N + r (host array); may
+ *       be NULL for DDP_VARIANT_VIEW.
  */
 int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs,
              int32_t N, int32_t variant, float scale, void* stream);

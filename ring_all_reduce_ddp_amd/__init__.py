@@ -5,7 +5,8 @@ The functions have the names of the C entry points in include/ddp_ring.h and
 only marshal arguments: torch tensors become device pointers, dtypes become
 DDP_FP32 / DDP_BF16, and the stream defaults to torch's current stream. Every
 step of the computation runs in the library's HIP kernels; there is no other
-code path. Importing this module fails if the library has not been built
+code path. The library is loaded on first use; every call fails with an
+ImportError naming the build command if it has not been built
 (python -m ring_all_reduce_ddp_amd.build).
 
 PyTorch is used for device memory and streams only. It is imported before the
@@ -31,7 +32,7 @@ DDP_BF16 = 1
 DDP_RS = 0
 DDP_AG = 1
 DDP_MAX_RANKS = 64
-VARIANTS = {"fused": 0, "steps": 1, "persistent": 2}
+VARIANTS = {"fused": 0, "steps": 1, "persistent": 2, "view": 3}
 
 _STATUS_NAMES = {DDP_EINVAL: "DDP_EINVAL", DDP_EHIP: "DDP_EHIP", DDP_ENORESOURCE: "DDP_ENORESOURCE",
                  DDP_ETIMEOUT: "DDP_ETIMEOUT", DDP_ENOMEM: "DDP_ENOMEM"}
@@ -70,6 +71,7 @@ def _load():
         "ddp_persistent_grid": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "ddp_persistent_status": (ctypes.c_int, [vp]),
         "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
+        "bucket_allreduce_view": (ctypes.c_int, [vp, i32, pp, i32, f32, vp]),
         "ddp_sync": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, vp]),
         "ddp_count_mismatches": (ctypes.c_int, [pp, i32, i64, i32, vp, vp]),
         "ddp_copy_probe": (ctypes.c_int, [vp, vp, i64, vp]),
@@ -81,12 +83,26 @@ def _load():
     return lib
 
 
-lib = _load()
+_lib = None
+
+
+def _get_lib():
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):
+    # `ring_all_reduce_ddp_amd.lib` is the ctypes handle, loaded on first access.
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def _check(status):
     if status != DDP_OK:
-        msg = lib.ddp_last_error()
+        msg = _get_lib().ddp_last_error()
         raise DDPError(status, msg.decode() if msg else "")
 
 
@@ -156,7 +172,7 @@ class Plan:
 
     def free(self):
         if self._h:
-            lib.ddp_plan_free(self._h)
+            _get_lib().ddp_plan_free(self._h)
             self._h = None
 
     def __del__(self):
@@ -168,17 +184,17 @@ class Plan:
     @property
     def num_buckets(self):
         n = ctypes.c_int32()
-        _check(lib.ddp_plan_num_buckets(self._h, ctypes.byref(n)))
+        _check(_get_lib().ddp_plan_num_buckets(self._h, ctypes.byref(n)))
         return n.value
 
     def bucket(self, b):
         """(padded_numel, [(param_index, offset, numel), ...]) of bucket b."""
         padded, nm = ctypes.c_int64(), ctypes.c_int32()
-        _check(lib.ddp_plan_bucket(self._h, b, ctypes.byref(padded), ctypes.byref(nm)))
+        _check(_get_lib().ddp_plan_bucket(self._h, b, ctypes.byref(padded), ctypes.byref(nm)))
         members = []
         for i in range(nm.value):
             p, off, m = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
-            _check(lib.ddp_plan_member(self._h, b, i, ctypes.byref(p), ctypes.byref(off), ctypes.byref(m)))
+            _check(_get_lib().ddp_plan_member(self._h, b, i, ctypes.byref(p), ctypes.byref(off), ctypes.byref(m)))
             members.append((p.value, off.value, m.value))
         return padded.value, members
 
@@ -194,7 +210,7 @@ class Plan:
         """(arena_numel, [offset of parameter p in elements])."""
         n = ctypes.c_int64()
         offs = (ctypes.c_int64 * max(self.n_params, 1))()
-        _check(lib.ddp_plan_grad_arena(self._h, ctypes.byref(n), offs))
+        _check(_get_lib().ddp_plan_grad_arena(self._h, ctypes.byref(n), offs))
         return n.value, list(offs[:self.n_params])
 
 
@@ -202,7 +218,7 @@ def ddp_bucket_plan(param_numels, dtype="fp32", cap_bytes=25 * 1024 * 1024,
                     first_bucket_bytes=1024 * 1024, world_size=1):
     numels = (ctypes.c_int64 * max(len(param_numels), 1))(*[int(m) for m in param_numels])
     h = ctypes.c_void_p()
-    _check(lib.ddp_bucket_plan(numels, len(param_numels), dtype_code(dtype), int(cap_bytes),
+    _check(_get_lib().ddp_bucket_plan(numels, len(param_numels), dtype_code(dtype), int(cap_bytes),
                                int(first_bucket_bytes), int(world_size), ctypes.byref(h)))
     return Plan(h.value, len(param_numels), dtype_code(dtype), int(world_size))
 
@@ -210,18 +226,18 @@ def ddp_bucket_plan(param_numels, dtype="fp32", cap_bytes=25 * 1024 * 1024,
 # ---------------------------------------------------------------- kernels
 
 def bucket_pack(plan, b, grad_arenas, bucket_bufs, stream=None):
-    _check(lib.bucket_pack(plan.handle, b, _ptr_array(grad_arenas), _ptr_array(bucket_bufs),
+    _check(_get_lib().bucket_pack(plan.handle, b, _ptr_array(grad_arenas), _ptr_array(bucket_bufs),
                            len(bucket_bufs), _stream(stream)))
 
 
 def bucket_unpack_scale(plan, b, bucket_bufs, grad_arenas, scale, stream=None):
-    _check(lib.bucket_unpack_scale(plan.handle, b, _ptr_array(bucket_bufs), _ptr_array(grad_arenas),
+    _check(_get_lib().bucket_unpack_scale(plan.handle, b, _ptr_array(bucket_bufs), _ptr_array(grad_arenas),
                                    len(bucket_bufs), float(scale), _stream(stream)))
 
 
 def ring_allreduce_step(bufs, step, phase, count=None, dtype=None, stream=None):
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
-    _check(lib.ring_allreduce_step(ptrs, n, count, dt, int(step), int(phase), _stream(stream)))
+    _check(_get_lib().ring_allreduce_step(ptrs, n, count, dt, int(step), int(phase), _stream(stream)))
 
 
 def ring_allreduce_stepwise(bufs, count=None, dtype=None, stream=None):
@@ -236,7 +252,7 @@ def ring_allreduce_persistent(bufs, n_steps=None, count=None, dtype=None, stream
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
     if n_steps is None:
         n_steps = 2 * (n - 1)
-    _check(lib.ring_allreduce_persistent(ptrs, n, count, dt, int(n_steps), _stream(stream)))
+    _check(_get_lib().ring_allreduce_persistent(ptrs, n, count, dt, int(n_steps), _stream(stream)))
 
 
 def ring_allreduce_persistent_ex(bufs, n_steps=None, max_blocks=0, timeout_us=10_000_000,
@@ -244,46 +260,55 @@ def ring_allreduce_persistent_ex(bufs, n_steps=None, max_blocks=0, timeout_us=10
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
     if n_steps is None:
         n_steps = 2 * (n - 1)
-    _check(lib.ring_allreduce_persistent_ex(ptrs, n, count, dt, int(n_steps), int(max_blocks),
+    _check(_get_lib().ring_allreduce_persistent_ex(ptrs, n, count, dt, int(n_steps), int(max_blocks),
                                             int(timeout_us), int(extra_arrivals), _stream(stream)))
 
 
 def ddp_persistent_grid(n, count, dtype="fp32"):
     """(grid, compute units) the persistent launch would use."""
     g, cu = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib.ddp_persistent_grid(int(n), int(count), dtype_code(dtype), ctypes.byref(g), ctypes.byref(cu)))
+    _check(_get_lib().ddp_persistent_grid(int(n), int(count), dtype_code(dtype), ctypes.byref(g), ctypes.byref(cu)))
     return g.value, cu.value
 
 
 def ddp_persistent_status(stream=None):
-    _check(lib.ddp_persistent_status(_stream(stream)))
+    _check(_get_lib().ddp_persistent_status(_stream(stream)))
 
 
 def ring_allreduce_fused(bufs, count=None, dtype=None, stream=None):
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
-    _check(lib.ring_allreduce_fused(ptrs, n, count, dt, _stream(stream)))
+    _check(_get_lib().ring_allreduce_fused(ptrs, n, count, dt, _stream(stream)))
 
 
-def ddp_sync(plan, grad_arenas, bucket_bufs, variant="fused", scale=None, stream=None):
+def bucket_allreduce_view(plan, b, grad_arenas, scale, stream=None):
+    _check(_get_lib().bucket_allreduce_view(plan.handle, b, _ptr_array(grad_arenas), len(grad_arenas),
+                                     float(scale), _stream(stream)))
+
+
+def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, stream=None):
     """bucket_bufs: list over buckets of lists over ranks (or a flat list,
-    bucket-major)."""
-    flat = [x for row in bucket_bufs for x in row] if isinstance(bucket_bufs[0], (list, tuple)) \
-        else list(bucket_bufs)
+    bucket-major); None for the "view" variant, which uses no bucket buffers."""
     n = len(grad_arenas)
+    if bucket_bufs is None:
+        bufs = None
+    else:
+        flat = [x for row in bucket_bufs for x in row] if isinstance(bucket_bufs[0], (list, tuple)) \
+            else list(bucket_bufs)
+        bufs = _ptr_array(flat)
     if scale is None:
         scale = 1.0 / n
-    _check(lib.ddp_sync(plan.handle, _ptr_array(grad_arenas), _ptr_array(flat), n,
-                        VARIANTS[variant], float(scale), _stream(stream)))
+    _check(_get_lib().ddp_sync(plan.handle, _ptr_array(grad_arenas), bufs, n, VARIANTS[variant], float(scale),
+                        _stream(stream)))
 
 
 def ddp_count_mismatches(bufs, out, count=None, dtype=None, stream=None):
     """Enqueues the count into `out` (a device int64/uint64 tensor of one element)."""
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
-    _check(lib.ddp_count_mismatches(ptrs, n, count, dt, ctypes.c_void_p(_ptr(out)), _stream(stream)))
+    _check(_get_lib().ddp_count_mismatches(ptrs, n, count, dt, ctypes.c_void_p(_ptr(out)), _stream(stream)))
 
 
 def ddp_copy_probe(dst, src, nbytes=None, stream=None):
     if nbytes is None:
         nbytes = src.numel() * src.element_size()
-    _check(lib.ddp_copy_probe(ctypes.c_void_p(_ptr(dst)), ctypes.c_void_p(_ptr(src)), int(nbytes),
+    _check(_get_lib().ddp_copy_probe(ctypes.c_void_p(_ptr(dst)), ctypes.c_void_p(_ptr(src)), int(nbytes),
                               _stream(stream)))

@@ -30,6 +30,16 @@ struct Segment {
   int64_t tile_begin;  // first pack tile of this segment (prefix sum)
 };
 
+// A run of one member's elements that lies inside one ring chunk of its
+// bucket: the unit of work of the in-place (bucket-view) sync.
+struct Piece {
+  int64_t src_off;     // offset in the gradient arena, elements (multiple of V)
+  int64_t numel;       // elements
+  int64_t tile_begin;  // first view tile of this piece (prefix sum)
+  int32_t chunk;       // ring chunk of the bucket that holds these elements
+  int32_t reserved;
+};
+
 struct Member {
   int32_t param;
   int64_t offset;
@@ -42,12 +52,17 @@ struct Bucket {
   int64_t seg_begin = 0;   // index of its first segment in plan.segments
   int64_t n_segs = 0;
   int64_t n_tiles = 0;     // pack/unpack tiles per rank
+  int64_t piece_begin = 0; // index of its first piece in plan.pieces
+  int64_t n_pieces = 0;
+  int64_t n_view_tiles = 0;
+  int64_t data_numel = 0;  // sum of its members' element counts
 };
 
 constexpr int kMaxDevices = 64;
 
 struct DeviceTable {
   Segment* segs = nullptr;   // device copy of plan.segments
+  Piece* pieces = nullptr;   // device copy of plan.pieces (same allocation)
 };
 
 }  // namespace ddp
@@ -62,6 +77,7 @@ struct ddp_plan {
   int64_t arena_numel = 0;
   std::vector<ddp::Bucket> buckets;
   std::vector<ddp::Segment> segments;   // all buckets' segments, bucket-major
+  std::vector<ddp::Piece> pieces;       // all buckets' pieces, bucket-major
   int64_t tile_elems = 0;               // elements per pack tile
   std::mutex mu;                        // guards `device`
   ddp::DeviceTable device[ddp::kMaxDevices];
@@ -75,6 +91,15 @@ constexpr int kPackVecsPerThread = 4;
 inline int64_t pack_tile_elems(int32_t dtype) {
   return int64_t(kPackThreads) * kPackVecsPerThread * (kVectorBytes / elem_bytes(dtype));
 }
+// Elements covered by one tile of the in-place sync: one wave, one 16-byte
+// vector per thread.
+constexpr int kViewThreads = 64;
+inline int64_t view_tile_elems(int32_t dtype) {
+  return int64_t(kViewThreads) * (kVectorBytes / elem_bytes(dtype));
+}
+// Device copies of the plan's segment and piece tables on the current
+// device, made on first use (defined with the HIP code).
+int device_tables(ddp_plan* plan, const Segment** segs, const Piece** pieces);
 // Releases the device tables of a plan (defined with the HIP code).
 void release_device_tables(ddp_plan* plan);
 }  // namespace ddp

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused_vec(RankPtrs P, int64_t
     fused_tile(tile, NR, tiles_per_chunk, FusedOrder<DT>::interleave, &c, &t);
     const int64_t lo = int64_t(c) * L;
     const int64_t hi = min(lo + L, count);
-    const int64_t vi = lo / V + t * kFusedThreads + threadIdx.x;
-    if (vi * V >= hi) continue;
+    const int64_t vi = tile_vector(lo, t, kFusedThreads, V);
+    if (vi * V < lo || vi * V >= hi) continue;
     // Ring order of chunk c: rank c+1 first, then c+2, ..., c.
     const void* src[NR];
 #pragma unroll
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused_vec_n(RankPtrs P, int n
     fused_tile(tile, n, tiles_per_chunk, FusedOrder<DT>::interleave, &c, &t);
     const int64_t lo = int64_t(c) * L;
     const int64_t hi = min(lo + L, count);
-    const int64_t vi = lo / V + t * kFusedThreads + threadIdx.x;
-    if (vi * V >= hi) continue;
+    const int64_t vi = tile_vector(lo, t, kFusedThreads, V);
+    if (vi * V < lo || vi * V >= hi) continue;
     const int first = wrap(c + 1, n);
     if ((vi + 1) * V <= hi) {
       typename O::Acc a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
@@ -147,8 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RankPtrs P, int n, in
 template <int DT, bool NTL>
 void launch_fused_vec(const RingArgs& a, hipStream_t s) {
   constexpr int V = Ops<DT>::V;
-  const int64_t tile = int64_t(kFusedThreads) * V;
-  const int64_t tpc = (a.L + tile - 1) / tile;
+  const int64_t tpc = aligned_tiles_per_chunk(a.L, int64_t(kFusedThreads) * V);
   const int64_t total = tpc * a.n;
   const dim3 g(grid_for(total)), b(kFusedThreads);
   switch (a.n) {

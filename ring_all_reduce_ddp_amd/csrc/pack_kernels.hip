@@ -87,32 +87,6 @@ __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, 
   }
 }
 
-// Device copy of the plan's segments on the current device (made once).
-int device_segments(ddp_plan* plan, const Segment** out) {
-  int dev = 0;
-  DDP_HIP_TRY(hipGetDevice(&dev), "plan tables: hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "plan tables: device index beyond 64");
-  std::lock_guard<std::mutex> lock(plan->mu);
-  DeviceTable& t = plan->device[dev];
-  if (t.segs == nullptr && !plan->segments.empty()) {
-    const size_t bytes = sizeof(Segment) * plan->segments.size();
-    void* p = nullptr;
-    hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(DDP_ENOMEM, std::string("plan tables: hipMalloc: ") + hipGetErrorString(e));
-    }
-    e = hipMemcpy(p, plan->segments.data(), bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      return hip_fail(e, "plan tables: hipMemcpy");
-    }
-    t.segs = static_cast<Segment*>(p);
-  }
-  *out = t.segs;
-  return DDP_OK;
-}
-
 bool spans_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return abytes > 0 && bbytes > 0 && x < y + uint64_t(bbytes) && y < x + uint64_t(abytes);
@@ -145,12 +119,43 @@ unsigned copy_grid(int64_t tiles) { return unsigned(std::max<int64_t>(1, std::mi
 
 }  // namespace
 
+int device_tables(ddp_plan* plan, const Segment** segs, const Piece** pieces) {
+  int dev = 0;
+  DDP_HIP_TRY(hipGetDevice(&dev), "plan tables: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "plan tables: device index beyond 64");
+  std::lock_guard<std::mutex> lock(plan->mu);
+  DeviceTable& t = plan->device[dev];
+  const size_t seg_bytes = sizeof(Segment) * plan->segments.size();
+  const size_t piece_bytes = sizeof(Piece) * plan->pieces.size();
+  if (t.segs == nullptr && seg_bytes + piece_bytes > 0) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, seg_bytes + piece_bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DDP_ENOMEM, std::string("plan tables: hipMalloc: ") + hipGetErrorString(e));
+    }
+    e = hipMemcpy(p, plan->segments.data(), seg_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess && piece_bytes > 0)
+      e = hipMemcpy(static_cast<char*>(p) + seg_bytes, plan->pieces.data(), piece_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "plan tables: hipMemcpy");
+    }
+    t.segs = static_cast<Segment*>(p);
+    t.pieces = reinterpret_cast<Piece*>(static_cast<char*>(p) + seg_bytes);
+  }
+  if (segs) *segs = t.segs;
+  if (pieces) *pieces = t.pieces;
+  return DDP_OK;
+}
+
 void release_device_tables(ddp_plan* plan) {
   std::lock_guard<std::mutex> lock(plan->mu);
   for (DeviceTable& t : plan->device) {
     if (t.segs != nullptr) {
       (void)hipFree(t.segs);
       t.segs = nullptr;
+      t.pieces = nullptr;
     }
   }
 }
@@ -167,7 +172,7 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   const Bucket& bk = plan->buckets[b];
   if (bk.n_tiles == 0) return DDP_OK;
   const Segment* segs = nullptr;
-  st = device_segments(const_cast<ddp_plan*>(plan), &segs);
+  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr);
   if (st != DDP_OK) return st;
   RankPtrs A{}, B{};
   for (int r = 0; r < N; ++r) {
@@ -192,7 +197,7 @@ extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* 
   const Bucket& bk = plan->buckets[b];
   if (bk.n_tiles == 0) return DDP_OK;
   const Segment* segs = nullptr;
-  st = device_segments(const_cast<ddp_plan*>(plan), &segs);
+  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr);
   if (st != DDP_OK) return st;
   RankPtrs A{}, B{};
   for (int r = 0; r < N; ++r) {
@@ -215,11 +220,19 @@ extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* co
                         int32_t N, int32_t variant, float scale, void* stream) {
   const char* fn = "ddp_sync";
   if (plan == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": plan is NULL");
-  if (grad_arenas == nullptr || bucket_bufs == nullptr)
-    return fail(DDP_EINVAL, std::string(fn) + ": pointer array is NULL");
-  if (variant != DDP_VARIANT_FUSED && variant != DDP_VARIANT_STEPS && variant != DDP_VARIANT_PERSISTENT)
+  if (variant != DDP_VARIANT_FUSED && variant != DDP_VARIANT_STEPS && variant != DDP_VARIANT_PERSISTENT &&
+      variant != DDP_VARIANT_VIEW)
     return fail(DDP_EINVAL, std::string(fn) + ": unknown variant");
+  if (grad_arenas == nullptr || (bucket_bufs == nullptr && variant != DDP_VARIANT_VIEW))
+    return fail(DDP_EINVAL, std::string(fn) + ": pointer array is NULL");
   if (N != plan->world_size) return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
+  if (variant == DDP_VARIANT_VIEW) {
+    for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
+      int st = bucket_allreduce_view(plan, b, grad_arenas, N, scale, stream);
+      if (st != DDP_OK) return st;
+    }
+    return DDP_OK;
+  }
   for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
     void* const* bufs = bucket_bufs + size_t(b) * N;
     const int64_t count = plan->buckets[b].padded_numel;

@@ -9,6 +9,7 @@
 // (blog.ans20xx.com), part "bucket 与 overlap", names the capacity an upper
 // limit: a tensor that would pass the capacity opens a new bucket, and one
 // larger than the capacity sits alone in its bucket.
+#include <algorithm>
 #include <new>
 
 #include "ddp_internal.h"
@@ -122,6 +123,32 @@ extern "C" int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, in
       }
       b.n_segs = int64_t(plan->segments.size()) - b.seg_begin;
       b.n_tiles = tiles;
+
+      // Pieces: each member cut at the bucket's ring-chunk boundaries
+      // (L = padded / N, a multiple of V), so a piece has one ring order.
+      b.piece_begin = int64_t(plan->pieces.size());
+      const int64_t L = b.padded_numel / world_size;
+      const int64_t vt = view_tile_elems(dtype);
+      int64_t vtiles = 0;
+      for (const Member& m : b.members) {
+        b.data_numel += m.numel;
+        for (int64_t pos = m.offset; pos < m.offset + m.numel;) {
+          const int64_t c = pos / L;
+          const int64_t end = std::min(m.offset + m.numel, (c + 1) * L);
+          Piece pc;
+          pc.src_off = plan->arena_offsets[m.param] + (pos - m.offset);
+          pc.numel = end - pos;
+          pc.tile_begin = vtiles;
+          pc.chunk = int32_t(c);
+          pc.reserved = 0;
+          // tiles on a grid aligned to whole tiles of the arena
+          vtiles += (pc.src_off + pc.numel + vt - 1) / vt - pc.src_off / vt;
+          plan->pieces.push_back(pc);
+          pos = end;
+        }
+      }
+      b.n_pieces = int64_t(plan->pieces.size()) - b.piece_begin;
+      b.n_view_tiles = vtiles;
     }
   } catch (const std::bad_alloc&) {
     delete plan;

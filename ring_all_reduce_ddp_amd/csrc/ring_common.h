@@ -39,6 +39,18 @@ inline int prepare(const char* fn, void* const* bufs, int32_t N, int64_t count, 
   return DDP_OK;
 }
 
+// Tiles of `tile` elements on a grid aligned to multiples of `tile` (not to
+// chunk starts): a chunk [lo, lo + L) is covered by the tiles that intersect
+// it, at most ceil(L / tile) + 1 of them.
+inline int64_t aligned_tiles_per_chunk(int64_t L, int64_t tile) { return (L + tile - 1) / tile + 1; }
+
+// Vector index handled by this thread in tile t of the chunk starting at
+// element lo (the first tile starts at lo rounded down to a whole tile).
+__device__ __forceinline__ int64_t tile_vector(int64_t lo, int64_t t, int threads, int V) {
+  const int64_t tile = int64_t(threads) * V;
+  return (lo / tile + t) * threads + threadIdx.x;
+}
+
 inline unsigned grid_for(int64_t total_tiles) {
   return unsigned(std::max<int64_t>(1, std::min(total_tiles, kMaxGrid)));
 }

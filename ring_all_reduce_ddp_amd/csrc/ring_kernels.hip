@@ -55,7 +55,9 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
   const int c = step_chunk(r, s, n, phase);
   const int64_t lo = int64_t(c) * L;
   const int64_t hi = min(lo + L, count);
-  const int64_t base = lo + (tile - int64_t(r) * tiles_per_chunk) * kTile;
+  // Tiles sit on a grid aligned to whole tiles (not to chunk starts), so
+  // waves touch whole cache lines even when chunks start between lines.
+  const int64_t base = (lo / kTile + (tile - int64_t(r) * tiles_per_chunk)) * kTile;
   if (base >= hi) return;
   const void* src = P.p[r];
   void* dst = P.p[wrap(r + 1, n)];
@@ -66,7 +68,7 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       vi[u] = base / V + int64_t(u) * T + threadIdx.x;
-      full[u] = (vi[u] + 1) * V <= hi;
+      full[u] = vi[u] * V >= lo && (vi[u] + 1) * V <= hi;
       if (full[u]) {
         a[u] = ld16<NT>(static_cast<const u32x4*>(src) + vi[u]);
         if (phase == DDP_RS) b[u] = ld16<NT>(static_cast<const u32x4*>(dst) + vi[u]);
@@ -82,7 +84,7 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
           y = O::to(acc);
         }
         st16<NT>(static_cast<u32x4*>(dst) + vi[u], y);
-      } else {
+      } else if (vi[u] * V >= lo) {
         const int64_t e0 = vi[u] * V;
         for (int64_t e = e0; e < hi && e < e0 + V; ++e) {
           const float x = O::load1(src, e);
@@ -92,7 +94,7 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
     }
   } else {
     const int64_t e = base + threadIdx.x;
-    if (e < hi) {
+    if (e >= lo && e < hi) {
       const float x = O::load1(src, e);
       O::store1(dst, e, phase == DDP_RS ? O::add1(x, O::load1(dst, e)) : x);
     }
@@ -180,13 +182,13 @@ __global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int6
 template <int DT>
 int64_t step_tiles_per_chunk(const RingArgs& a) {
   const int64_t tile = a.vec ? int64_t(kThreads) * kStepUnroll * Ops<DT>::V : kThreads;
-  return (a.L + tile - 1) / tile;
+  return aligned_tiles_per_chunk(a.L, tile);
 }
 
 template <int DT, bool VEC, bool NT>
 int launch_step_impl(const RingArgs& a, int step, int phase, hipStream_t s) {
   const int64_t tile = VEC ? int64_t(kStepThreads) * Ops<DT>::V : kStepThreads;
-  const int64_t tpc = (a.L + tile - 1) / tile;
+  const int64_t tpc = aligned_tiles_per_chunk(a.L, tile);
   const int64_t total = tpc * a.n;
   const dim3 g(grid_for(total)), b(kStepThreads);
   if (phase == DDP_RS)

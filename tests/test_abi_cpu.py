@@ -126,3 +126,28 @@ def test_ring_argument_errors_before_launch():
     expect_status(lib.ddp_sync(p.handle, bufs, bufs, 2, 9, 0.5, None), rar.DDP_EINVAL, "variant")
     # zero-length work is accepted without touching the device
     assert lib.ring_allreduce_fused(bufs, 2, 0, rar.DDP_FP32, None) == rar.DDP_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library every entry point raises an ImportError that
+    names the build command; nothing falls back to another implementation."""
+    monkeypatch.setattr(rar, "LIB_PATH", "/nonexistent/libddp_ring.so")
+    monkeypatch.setattr(rar, "_lib", None)
+    with pytest.raises(ImportError, match="ring_all_reduce_ddp_amd.build"):
+        rar.ddp_bucket_plan([4, 8], "fp32")
+    with pytest.raises(ImportError):
+        rar.lib
+
+
+def test_view_sync_argument_errors():
+    lib = rar.lib
+    p = rar.ddp_bucket_plan([4, 8], "fp32", world_size=2)
+    bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    expect_status(lib.bucket_allreduce_view(p.handle, 3, bufs, 2, 0.5, None), rar.DDP_EINVAL, "out of range")
+    expect_status(lib.bucket_allreduce_view(p.handle, 0, bufs, 4, 0.5, None), rar.DDP_EINVAL, "world size")
+    expect_status(lib.bucket_allreduce_view(None, 0, bufs, 2, 0.5, None), rar.DDP_EINVAL, "plan is NULL")
+    odd = (ctypes.c_void_p * 2)(0x1008, 0x2000)
+    expect_status(lib.bucket_allreduce_view(p.handle, 0, odd, 2, 0.5, None), rar.DDP_EINVAL, "aligned")
+    # the view variant of ddp_sync needs no bucket buffers
+    expect_status(lib.ddp_sync(p.handle, odd, None, 2, 3, 0.5, None), rar.DDP_EINVAL, "aligned")
+    expect_status(lib.ddp_sync(p.handle, bufs, None, 2, 0, 0.5, None), rar.DDP_EINVAL, "NULL")

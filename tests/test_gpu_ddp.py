@@ -101,22 +101,46 @@ def oracle_sync(grads, numels, n, dtype="fp32"):
     return ddp.ddp_sync(grads, oplan, dtype)
 
 
-@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
-def test_small_sync_against_oracle(variant):
-    numels = [7, 16, 1, 40, 3, 300, 9, 0, 5000, 33, 12345, 2]
-    n = 4
-    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=8192, first_bucket_bytes=256, world_size=n)
-    grads = host_grads(23, n, numels)
-    arenas, offs = make_arenas(plan, grads, "fp32")
-    buckets = bucket_buffers(plan, n, "fp32")
-    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+ALL_VARIANTS = ["fused", "steps", "persistent", "view"]
+
+
+def sync_case(variant, n, dtype, numels, cap, first, seed, scale=None):
+    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+    grads = host_grads(seed, n, numels)
+    if dtype == "bf16":
+        from ddp_workloads.gen import to_bf16_bits
+        grads = [[to_bf16_bits(x) for x in g] for g in grads]
+        grads_f32 = [[(x.astype(np.uint32) << 16).view(np.float32) for x in g] for g in grads]
+    else:
+        grads_f32 = grads
+    arenas, offs = make_arenas(plan, grads_f32, dtype)
+    buckets = None if variant == "view" else bucket_buffers(plan, n, dtype)
+    rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=scale)
     torch.cuda.synchronize()
-    got = read_grads(arenas, offs, numels, "fp32")
-    oplan = planner.plan(numels, 4, 8192, 256, n)
-    want = ddp.ddp_sync(grads, oplan, "fp32")
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+    got = read_grads(arenas, offs, numels, dtype)
+    oplan = planner.plan(numels, 4 if dtype == "fp32" else 2, cap, first, n)
+    want = ddp.ddp_sync(grads, oplan, dtype, scale=scale)
     for r in range(n):
         for p in range(len(numels)):
-            assert_bit_equal(got[r][p], want[r][p], f"{variant} r{r} p{p}")
+            assert_bit_equal(got[r][p], want[r][p], f"{variant} n={n} {dtype} rank {r} param {p}")
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+def test_small_sync_against_oracle(variant):
+    numels = [7, 16, 1, 40, 3, 300, 9, 0, 5000, 33, 12345, 2]
+    sync_case(variant, 4, "fp32", numels, 8192, 256, seed=23)
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 9, 16])
+def test_sync_ranks_and_dtypes(variant, dtype, n):
+    """Members that straddle ring-chunk boundaries, one-element and empty
+    parameters, several buckets; scale = fl(1/N)."""
+    numels = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5]
+    sync_case(variant, n, dtype, numels, 64 * 1024, 512, seed=40 + n)
 
 
 @pytest.fixture(scope="module")
@@ -128,7 +152,7 @@ def resnet50_case():
     return w, numels, grads, want
 
 
-@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
 def test_resnet50_sync(resnet50_case, variant):
     """The full sync of ResNet-50 gradients over 8 ranks: reverse-order buckets
     (1 MiB first, 25 MiB cap), pack, all-reduce, x1/8, unpack."""
@@ -136,7 +160,7 @@ def test_resnet50_sync(resnet50_case, variant):
     plan = rar.ddp_bucket_plan(numels, "fp32", world_size=w.n)
     assert plan.num_buckets == 6
     arenas, offs = make_arenas(plan, grads, "fp32")
-    buckets = bucket_buffers(plan, w.n, "fp32")
+    buckets = None if variant == "view" else bucket_buffers(plan, w.n, "fp32")
     rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=0.125)
     torch.cuda.synchronize()
     got = read_grads(arenas, offs, numels, "fp32")
