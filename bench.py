@@ -7,8 +7,9 @@ Reported: bus bandwidth 2(N-1)/N * S / t (the per-rank traffic of a ring
 all-reduce), algorithm bandwidth S / t, and the HBM bandwidth of the kernel,
 2 * N * S / t, against MI355X's 8 TB/s.
 
-Beside it, in the same run: the step-by-step and persistent forms and the
-bf16 buffers of the same workload, a copy probe, the whole DDP sync of
+Beside it, in the same run: the step-by-step and persistent forms, the
+reduce-scatter output alone, and the bf16 buffers of the same workload, a
+copy probe, the whole DDP sync of
 ResNet-50 gradients (8 ranks), the 64-rank 300M-element workload, and the CPU
 oracle timed on the headline workload's own inputs.
 
@@ -138,7 +139,16 @@ def main():
                         "hbm_frac_of_peak": round(gbps(step_bytes, t) / PEAK_HBM_GBPS, 4),
                         "launches": 2 * (n - 1) if name == "steps" else 1}
     rar.ddp_persistent_status()
-    del bufs
+
+    # reduce-scatter output (each rank's 1/N shard, scaled by 1/N): reads N*S, writes S
+    shards = [torch.empty(count // n, device="cuda") for _ in range(n)]
+    rar.ring_reduce_scatter_fused(bufs, shards, 1.0 / n)
+    t = time_launches(lambda: rar.ring_reduce_scatter_fused(bufs, shards, 1.0 / n), reps, torch)
+    rs_bytes = (n + 1) * S
+    extras["reduce_scatter_fused"] = {"ms": round(t, 4), "hbm_gbps": round(gbps(rs_bytes, t), 1),
+                                      "hbm_frac_of_peak": round(gbps(rs_bytes, t) / PEAK_HBM_GBPS, 4),
+                                      "bus_gbps_rs_phase": round(gbps((n - 1) / n * S, t), 1)}
+    del bufs, shards
     torch.cuda.empty_cache()
 
     bb = device_ring_inputs(w.seed, n, 2 * count, "bf16", std=w.std)

@@ -222,6 +222,23 @@ int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dt
 int bucket_allreduce_view(const ddp_plan* plan, int32_t b, void* const* grad_arenas, int32_t N,
                           float scale, void* stream);
 
+/* ring_reduce_scatter_fused: the reduce-scatter phase alone, as its output:
+ * every rank's gradient shard ([R] section 03: after the N-1 reduce-scatter
+ * steps each rank holds one fully reduced chunk; [X] §1.3.2.1: chunk r on rank
+ * r; [R] section 07: sharded data parallelism keeps such a shard per rank).
+ * For every chunk c: shards[c][i] = rnd(scale * sum), where sum adds the N
+ * ranks' element c*L+i in ring order (rank c+1 first, then c+2, ..., c, one
+ * rounding per add) -- the value the N-1 reduce-scatter steps leave on rank c.
+ *   bufs[N]: device pointers to the N input buffers (count elements each,
+ *       element-aligned, pairwise disjoint); read only.
+ *   shards[N]: device pointers; shards[c] receives chunk c's
+ *       min(L, count - c*L) elements (L = ceil(count/N)); may be NULL for an
+ *       empty chunk; must not overlap the inputs or each other.
+ *   scale: fp32 multiplier (1 for the sum, 1/N for the mean).
+ * Reads N*S bytes and writes S. */
+int ring_reduce_scatter_fused(const void* const* bufs, void* const* shards, int32_t N, int64_t count,
+                              int32_t dtype, float scale, void* stream);
+
 /* ---------------------------------------------------------------- whole sync
  * ddp_sync: one DDP gradient synchronisation. For every bucket b in plan
  * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_FUSED,

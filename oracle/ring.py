@@ -179,6 +179,30 @@ def ring_order_sum(x, c, dtype):
     return acc
 
 
+def reduce_scatter(bufs, dtype, scale=1.0):
+    """Reduce-scatter output of the ring: the gradient shard of every rank.
+
+    Runs the reduce-scatter phase (the first N-1 steps; page "DDP 与 Ring
+    All-Reduce", blog.vllbc.top, section 03: after it every rank holds one
+    chunk reduced over all ranks; page "DDP 与 Ring-AllReduce",
+    xuesongtap.github.io, §1.3.2.1: that chunk is chunk r on rank r), then
+    returns, for each rank r, its chunk r multiplied by the fp32 value `scale`
+    with one rounding to the dtype (scale = 1/N gives the mean, as DDP's
+    division by the world size). This is the gradient shard that sharded data
+    parallelism keeps (page "DDP 与 Ring All-Reduce", section 07, the part on
+    FSDP/ZeRO). Returns a list of N arrays; rank r's has the length of chunk r.
+    """
+    n = len(bufs)
+    after = ring_simulate(bufs, dtype, n_steps=n - 1)["bufs"]
+    count = len(after[0])
+    s = float(np.float32(scale))
+    out = []
+    for r in range(n):
+        lo, hi = chunk_bounds(count, n, r)
+        out.append(rounding.round_to(rounding.to_f64(after[r][lo:hi], dtype) * s, dtype))
+    return out
+
+
 def sum_f64(bufs, dtype):
     """Per-element sum of the exact input values, correctly rounded to float64
     (Python's math.fsum per element; small inputs only)."""

@@ -72,6 +72,7 @@ def _load():
         "ddp_persistent_status": (ctypes.c_int, [vp]),
         "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
         "bucket_allreduce_view": (ctypes.c_int, [vp, i32, pp, i32, f32, vp]),
+        "ring_reduce_scatter_fused": (ctypes.c_int, [pp, pp, i32, i64, i32, f32, vp]),
         "ddp_sync": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, vp]),
         "ddp_count_mismatches": (ctypes.c_int, [pp, i32, i64, i32, vp, vp]),
         "ddp_copy_probe": (ctypes.c_int, [vp, vp, i64, vp]),
@@ -283,6 +284,14 @@ def ring_allreduce_fused(bufs, count=None, dtype=None, stream=None):
 def bucket_allreduce_view(plan, b, grad_arenas, scale, stream=None):
     _check(_get_lib().bucket_allreduce_view(plan.handle, b, _ptr_array(grad_arenas), len(grad_arenas),
                                      float(scale), _stream(stream)))
+
+
+def ring_reduce_scatter_fused(bufs, shards, scale=1.0, count=None, dtype=None, stream=None):
+    """shards[c] receives chunk c of the ring sum (times scale); None for an
+    empty chunk."""
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    sh = (ctypes.c_void_p * n)(*[None if x is None else _ptr(x) for x in shards])
+    _check(_get_lib().ring_reduce_scatter_fused(ptrs, sh, n, count, dt, float(scale), _stream(stream)))
 
 
 def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, stream=None):

@@ -1,0 +1,182 @@
+// Reduce-scatter output of the ring: every rank's gradient shard.
+//
+// Page "DDP 与 Ring All-Reduce" (blog.vllbc.top), section 03: after the N-1
+// reduce-scatter steps each rank holds one chunk reduced over all ranks; page
+// "DDP 与 Ring-AllReduce" (xuesongtap.github.io), §1.3.2.1: that chunk is chunk
+// r on rank r. Section 07 of the first page separates DDP (every rank keeps
+// the whole gradient) from FSDP/ZeRO (each rank keeps a shard); the shard is
+// what the reduce-scatter phase alone produces.
+//
+// One pass: each element of chunk c is read once from every rank, summed in
+// the order the hops add it (rank c+1 first, then c+2, ..., c; one rounding
+// per add), multiplied by `scale` (one rounding) and written to rank c's
+// shard. N*S bytes are read and S written; the input buffers are not
+// modified. Launch shape and tile grid as for the fused all-reduce.
+#include <algorithm>
+
+#include "ring_common.h"
+
+namespace ddp {
+namespace {
+
+constexpr int kScatterThreads = 64;
+constexpr int kScatterBatch = 16;
+constexpr int64_t kScatterCacheResidentBytes = int64_t(256) << 20;
+
+// NR > 0: compile-time rank count; NR == 0: any N, loaded kScatterBatch at a time.
+template <int DT, int NR, bool NTL>
+__global__ __launch_bounds__(kScatterThreads) void k_scatter_vec(RankPtrs P, RankPtrs S, int n_rt, int64_t count,
+                                                                 int64_t L, int64_t tiles_per_chunk,
+                                                                 int64_t total_tiles, float scale) {
+  using O = Ops<DT>;
+  constexpr int V = O::V;
+  const int n = NR > 0 ? NR : n_rt;
+  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    const int c = int(tile / tiles_per_chunk);
+    const int64_t t = tile - int64_t(c) * tiles_per_chunk;
+    const int64_t lo = int64_t(c) * L;
+    const int64_t hi = min(lo + L, count);
+    const int64_t vi = tile_vector(lo, t, kScatterThreads, V);
+    if (vi * V < lo || vi * V >= hi) continue;
+    const int first = wrap(c + 1, n);
+    void* shard = S.p[c];
+    if ((vi + 1) * V <= hi) {
+      typename O::Acc a;
+      if constexpr (NR > 0) {
+        u32x4 x[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) x[k] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k, NR)]) + vi);
+        a = O::from(x[0]);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) O::add(a, x[k]);
+      } else {
+        a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
+        for (int k = 1; k < n; k += kScatterBatch) {
+          u32x4 x[kScatterBatch];
+#pragma unroll
+          for (int j = 0; j < kScatterBatch; ++j)
+            if (k + j < n) x[j] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
+#pragma unroll
+          for (int j = 0; j < kScatterBatch; ++j)
+            if (k + j < n) O::add(a, x[j]);
+        }
+      }
+      st16<true>(static_cast<u32x4*>(shard) + (vi - lo / V), O::scale(O::to(a), scale));
+    } else {
+      for (int64_t e = vi * V; e < hi; ++e) {
+        float acc = O::load1(P.p[first], e);
+        for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
+        O::store1(shard, e - lo, O::mul1(acc, scale));
+      }
+    }
+  }
+}
+
+// Fallback for chunks that do not start on 16-byte boundaries: one element per thread.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_scatter_scalar(RankPtrs P, RankPtrs S, int n, int64_t count, int64_t L,
+                                                             int64_t tiles_per_chunk, int64_t total_tiles,
+                                                             float scale) {
+  using O = Ops<DT>;
+  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    const int c = int(tile / tiles_per_chunk);
+    const int64_t lo = int64_t(c) * L;
+    const int64_t hi = min(lo + L, count);
+    const int64_t e = lo + (tile - int64_t(c) * tiles_per_chunk) * kThreads + threadIdx.x;
+    if (e >= hi) continue;
+    const int first = wrap(c + 1, n);
+    float acc = O::load1(P.p[first], e);
+    for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
+    O::store1(S.p[c], e - lo, O::mul1(acc, scale));
+  }
+}
+
+template <int DT, bool NTL>
+void launch_scatter_vec(const RingArgs& a, const RankPtrs& S, float scale, hipStream_t s) {
+  constexpr int V = Ops<DT>::V;
+  const int64_t tpc = aligned_tiles_per_chunk(a.L, int64_t(kScatterThreads) * V);
+  const int64_t total = tpc * a.n;
+  const dim3 g(grid_for(total)), b(kScatterThreads);
+  switch (a.n) {
+#define DDP_SCATTER_CASE(NR)                                                                                  \
+  case NR:                                                                                                    \
+    hipLaunchKernelGGL((k_scatter_vec<DT, NR, NTL>), g, b, 0, s, a.P, S, a.n, a.count, a.L, tpc, total, scale); \
+    break;
+    DDP_SCATTER_CASE(1)
+    DDP_SCATTER_CASE(2)
+    DDP_SCATTER_CASE(3)
+    DDP_SCATTER_CASE(4)
+    DDP_SCATTER_CASE(5)
+    DDP_SCATTER_CASE(6)
+    DDP_SCATTER_CASE(7)
+    DDP_SCATTER_CASE(8)
+#undef DDP_SCATTER_CASE
+    default:
+      hipLaunchKernelGGL((k_scatter_vec<DT, 0, NTL>), g, b, 0, s, a.P, S, a.n, a.count, a.L, tpc, total, scale);
+  }
+}
+
+template <int DT>
+int launch_scatter(const RingArgs& a, const RankPtrs& S, bool shards_aligned, float scale, hipStream_t s) {
+  if (a.vec && shards_aligned) {
+    if (int64_t(a.n) * a.count * elem_bytes(DT) > kScatterCacheResidentBytes)
+      launch_scatter_vec<DT, true>(a, S, scale, s);
+    else
+      launch_scatter_vec<DT, false>(a, S, scale, s);
+  } else {
+    const int64_t tpc = (a.L + kThreads - 1) / kThreads;
+    const int64_t total = tpc * a.n;
+    hipLaunchKernelGGL((k_scatter_scalar<DT>), dim3(grid_for(total)), dim3(kThreads), 0, s, a.P, S, a.n, a.count,
+                       a.L, tpc, total, scale);
+  }
+  DDP_HIP_TRY(hipGetLastError(), "ring_reduce_scatter_fused: launch");
+  return DDP_OK;
+}
+
+}  // namespace
+}  // namespace ddp
+
+using namespace ddp;
+
+extern "C" int ring_reduce_scatter_fused(const void* const* bufs, void* const* shards, int32_t N, int64_t count,
+                                         int32_t dtype, float scale, void* stream) {
+  const char* fn = "ring_reduce_scatter_fused";
+  RingArgs a;
+  int st = prepare(fn, const_cast<void* const*>(bufs), N, count, dtype, &a);
+  if (st != DDP_OK) return st;
+  if (shards == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": shards array is NULL");
+  const int eb = elem_bytes(dtype);
+  bool aligned = true;
+  for (int c = 0; c < N; ++c) {
+    const int64_t lo = std::min<int64_t>(int64_t(c) * a.L, count);
+    const int64_t len = std::min<int64_t>(lo + a.L, count) - lo;
+    const std::string name = "shards[" + std::to_string(c) + "]";
+    if (len == 0) continue;
+    if (shards[c] == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is NULL");
+    if (reinterpret_cast<uintptr_t>(shards[c]) % uintptr_t(eb) != 0)
+      return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is not element-aligned");
+    aligned = aligned && reinterpret_cast<uintptr_t>(shards[c]) % 16 == 0;
+    st = check_range(shards[c], len * eb, fn, name.c_str());
+    if (st != DDP_OK) return st;
+    // a shard must not overlap any input buffer or another shard
+    const uintptr_t x = reinterpret_cast<uintptr_t>(shards[c]);
+    for (int r = 0; r < N; ++r) {
+      const uintptr_t y = reinterpret_cast<uintptr_t>(bufs[r]);
+      if (count > 0 && x < y + uint64_t(count * eb) && y < x + uint64_t(len * eb))
+        return fail(DDP_EINVAL, std::string(fn) + ": " + name + " overlaps bufs[" + std::to_string(r) + "]");
+      if (r != c && r < N) {
+        const int64_t lo2 = std::min<int64_t>(int64_t(r) * a.L, count);
+        const int64_t len2 = std::min<int64_t>(lo2 + a.L, count) - lo2;
+        const uintptr_t z = reinterpret_cast<uintptr_t>(shards[r]);
+        if (len2 > 0 && shards[r] != nullptr && x < z + uint64_t(len2 * eb) && z < x + uint64_t(len * eb))
+          return fail(DDP_EINVAL, std::string(fn) + ": " + name + " overlaps shards[" + std::to_string(r) + "]");
+      }
+    }
+  }
+  if (count == 0) return DDP_OK;
+  RankPtrs S{};
+  for (int c = 0; c < N; ++c) S.p[c] = shards[c];
+  hipStream_t s = as_stream(stream);
+  return dtype == DDP_FP32 ? launch_scatter<DDP_FP32>(a, S, aligned, scale, s)
+                           : launch_scatter<DDP_BF16>(a, S, aligned, scale, s);
+}

@@ -151,3 +151,14 @@ def test_view_sync_argument_errors():
     # the view variant of ddp_sync needs no bucket buffers
     expect_status(lib.ddp_sync(p.handle, odd, None, 2, 3, 0.5, None), rar.DDP_EINVAL, "aligned")
     expect_status(lib.ddp_sync(p.handle, bufs, None, 2, 0, 0.5, None), rar.DDP_EINVAL, "NULL")
+
+
+def test_reduce_scatter_argument_errors():
+    lib = rar.lib
+    bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    shards = (ctypes.c_void_p * 2)(0x3000, 0x4000)
+    expect_status(lib.ring_reduce_scatter_fused(bufs, None, 2, 0, rar.DDP_FP32, 1.0, None), rar.DDP_EINVAL, "shards")
+    expect_status(lib.ring_reduce_scatter_fused(bufs, shards, 0, 10, rar.DDP_FP32, 1.0, None), rar.DDP_EINVAL, "N must")
+    odd = (ctypes.c_void_p * 2)(0x3001, 0x4000)
+    # empty buffers: nothing to check or launch
+    assert lib.ring_reduce_scatter_fused(bufs, odd, 2, 0, rar.DDP_FP32, 1.0, None) == rar.DDP_OK

@@ -196,3 +196,33 @@ def test_error_bound_is_reached_in_part():
 def test_fsum_helper_is_exactly_rounded():
     assert ring.sum_f64([np.array([1e8], np.float32), np.array([1.0], np.float32),
                          np.array([-1e8], np.float32)], "fp32")[0] == math.fsum([1e8, 1.0, -1e8])
+
+
+# ---------------------------------------------------------------- reduce-scatter output
+
+@pytest.mark.parametrize("n,count", [(1, 5), (2, 8), (3, 6), (4, 10), (8, 64), (8, 3), (9, 100)])
+def test_reduce_scatter_integer_shards(n, count):
+    """Integer inputs: rank r's shard is exactly the sum of chunk r over all
+    ranks (times a power-of-two scale, also exact)."""
+    bufs = int_inputs(n, count, -1000, 1000, 300 + n, "fp32")
+    total = np.sum(np.stack(bufs).astype(np.int64), axis=0)
+    for scale, div in ((1.0, 1), (0.25, 4)):
+        shards = ring.reduce_scatter(bufs, "fp32", scale)
+        assert len(shards) == n
+        for r in range(n):
+            lo, hi = ring.chunk_bounds(count, n, r)
+            assert np.array_equal(shards[r].astype(np.float64), total[lo:hi] / div)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_reduce_scatter_matches_closed_form(dtype):
+    """The shards equal the ring-order sum of each chunk, scaled and rounded once."""
+    n, count = 5, 5 * 37 + 2
+    bufs = host_ring_inputs(12, n, count, dtype, std=1e-2)
+    s = np.float32(1) / np.float32(n)
+    shards = ring.reduce_scatter(bufs, dtype, s)
+    for c in range(n):
+        lo, hi = ring.chunk_bounds(count, n, c)
+        x = np.stack([b[lo:hi] for b in bufs])
+        want = rounding.round_to(rounding.to_f64(ring.ring_order_sum(x, c, dtype), dtype) * float(s), dtype)
+        assert np.array_equal(shards[c].view(np.uint8), want.view(np.uint8))
