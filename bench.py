@@ -195,8 +195,16 @@ def main():
             # pack + fused + unpack move 6*N*S; the in-place sync 2*N*S (padding excluded)
             sync_bytes = (2 if variant == "view" else 6) * wr.n * grad_bytes
             sync[variant]["hbm_gbps_algorithmic"] = round(gbps(sync_bytes, t), 1)
+    # the bf16 compression hook: fp32 gradients through bf16 buckets
+    cplan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=wr.n)
+    cbuckets = [[torch.empty(cplan.bucket(b)[0], dtype=torch.bfloat16, device="cuda") for _ in range(wr.n)]
+                for b in range(cplan.num_buckets)]
+    rar.ddp_sync(cplan, arenas, cbuckets, variant="fused")
+    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, cbuckets, variant="fused"), reps, torch)
+    sync["bf16_compressed_fused"] = {"ms": round(t, 4),
+                                     "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
     extras["ddp_sync_resnet50_n8"] = sync
-    del arenas, buckets
+    del arenas, buckets, cbuckets
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ 64 ranks x 300M fp32

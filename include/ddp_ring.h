@@ -106,6 +106,20 @@ int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, int32_t dtype
                     int64_t cap_bytes, int64_t first_bucket_bytes, int32_t world_size,
                     ddp_plan** out);
 
+/* ddp_bucket_plan_ex: as ddp_bucket_plan, with gradients and buckets in
+ * different dtypes. grad_dtype lays out the gradient arena and is the unit of
+ * the capacities (DDP forms buckets over the gradients); comm_dtype is the
+ * buckets' dtype: members start at multiples of its 16-byte vector and the
+ * ring runs in it. The supported pairs are equal dtypes and fp32 gradients in
+ * bf16 buckets: the bf16 compression hook ([D] reading list, "PyTorch DDP
+ * Communication Hooks"), in which bucket_pack rounds every gradient to bf16
+ * (nearest, ties to even), the ring adds in bf16 with one rounding per hop,
+ * and bucket_unpack_scale widens to fp32 and rounds scale * value once. The
+ * in-place sync (bucket_allreduce_view) needs equal dtypes. */
+int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params, int32_t grad_dtype,
+                       int32_t comm_dtype, int64_t cap_bytes, int64_t first_bucket_bytes,
+                       int32_t world_size, ddp_plan** out);
+
 /* Releases a plan and its device tables (NULL is accepted). Must not be
  * called while work that uses the plan is still running. */
 void ddp_plan_free(ddp_plan* plan);
@@ -132,9 +146,11 @@ int ddp_plan_grad_arena(const ddp_plan* plan, int64_t* arena_numel, int64_t* par
  * (the gradient-to-bucket copy of DDP's default gradient_as_bucket_view=False,
  * [R] sections 03 and 05).
  *   grad_arenas[N]: device pointers, 16-byte aligned, each holding one rank's
- *       arena as laid out by ddp_plan_grad_arena (arena_numel elements).
+ *       arena as laid out by ddp_plan_grad_arena (arena_numel elements of the
+ *       gradients' dtype).
  *   bucket_bufs[N]: device pointers, 16-byte aligned, each padded_numel
- *       elements of bucket b; positions not covered by a member are zeroed.
+ *       elements (of the buckets' dtype) of bucket b; positions not covered
+ *       by a member are zeroed.
  *   N must equal the plan's world size.
  */
 int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* grad_arenas,

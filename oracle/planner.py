@@ -50,14 +50,20 @@ def bucket_capacity(index, cap_bytes, first_bucket_bytes):
 
 
 def plan(param_numels, elem_bytes, cap_bytes=DEFAULT_CAP_BYTES,
-         first_bucket_bytes=DEFAULT_FIRST_BUCKET_BYTES, world_size=1):
+         first_bucket_bytes=DEFAULT_FIRST_BUCKET_BYTES, world_size=1, vector_elems=None):
     """Assign parameters to buckets.
 
     param_numels       : element counts of the parameters, in registration order.
-    elem_bytes         : 4 (fp32) or 2 (bf16).
+    elem_bytes         : 4 (fp32) or 2 (bf16): the gradients' element size, in
+                         which capacities are counted.
     cap_bytes          : capacity of every bucket after the first.
     first_bucket_bytes : capacity of bucket 0.
     world_size         : N, used only for the padding of each bucket.
+    vector_elems       : alignment of members and padding, in elements; by
+                         default one 16-byte vector of the gradient dtype. A
+                         bucket communicated in a narrower dtype (the bf16
+                         compression of fp32 gradients) uses that dtype's
+                         vector: 8 elements.
 
     Returns a list of buckets in launch order; each bucket is a dict with
       "members": list of (param_index, offset, numel), offsets in elements,
@@ -67,7 +73,9 @@ def plan(param_numels, elem_bytes, cap_bytes=DEFAULT_CAP_BYTES,
         raise ValueError("elem_bytes must be 2 or 4")
     if cap_bytes <= 0 or first_bucket_bytes <= 0 or world_size < 1:
         raise ValueError("capacities and world size must be positive")
-    v = VECTOR_BYTES // elem_bytes
+    v = VECTOR_BYTES // elem_bytes if vector_elems is None else int(vector_elems)
+    if v < 1:
+        raise ValueError("vector_elems must be positive")
     buckets = []
     members = []
     used = 0  # elements used in the open bucket, multiple of v

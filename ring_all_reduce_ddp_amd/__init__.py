@@ -57,6 +57,8 @@ def _load():
         "ddp_last_error": (ctypes.c_char_p, []),
         "ddp_bucket_plan": (ctypes.c_int, [ctypes.POINTER(i64), i32, i32, i64, i64, i32,
                                            ctypes.POINTER(vp)]),
+        "ddp_bucket_plan_ex": (ctypes.c_int, [ctypes.POINTER(i64), i32, i32, i32, i64, i64, i32,
+                                              ctypes.POINTER(vp)]),
         "ddp_plan_free": (None, [vp]),
         "ddp_plan_num_buckets": (ctypes.c_int, [vp, ctypes.POINTER(i32)]),
         "ddp_plan_bucket": (ctypes.c_int, [vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]),
@@ -165,6 +167,7 @@ class Plan:
         self._h = handle
         self.n_params = n_params
         self.dtype = dtype
+        self.comm_dtype = dtype
         self.world_size = world_size
 
     @property
@@ -220,8 +223,20 @@ def ddp_bucket_plan(param_numels, dtype="fp32", cap_bytes=25 * 1024 * 1024,
     numels = (ctypes.c_int64 * max(len(param_numels), 1))(*[int(m) for m in param_numels])
     h = ctypes.c_void_p()
     _check(_get_lib().ddp_bucket_plan(numels, len(param_numels), dtype_code(dtype), int(cap_bytes),
-                               int(first_bucket_bytes), int(world_size), ctypes.byref(h)))
+                                      int(first_bucket_bytes), int(world_size), ctypes.byref(h)))
     return Plan(h.value, len(param_numels), dtype_code(dtype), int(world_size))
+
+
+def ddp_bucket_plan_ex(param_numels, grad_dtype="fp32", comm_dtype="bf16", cap_bytes=25 * 1024 * 1024,
+                       first_bucket_bytes=1024 * 1024, world_size=1):
+    numels = (ctypes.c_int64 * max(len(param_numels), 1))(*[int(m) for m in param_numels])
+    h = ctypes.c_void_p()
+    _check(_get_lib().ddp_bucket_plan_ex(numels, len(param_numels), dtype_code(grad_dtype),
+                                         dtype_code(comm_dtype), int(cap_bytes), int(first_bucket_bytes),
+                                         int(world_size), ctypes.byref(h)))
+    plan = Plan(h.value, len(param_numels), dtype_code(grad_dtype), int(world_size))
+    plan.comm_dtype = dtype_code(comm_dtype)
+    return plan
 
 
 # ---------------------------------------------------------------- kernels

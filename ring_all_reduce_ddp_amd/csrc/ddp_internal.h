@@ -68,7 +68,8 @@ struct DeviceTable {
 }  // namespace ddp
 
 struct ddp_plan {
-  int32_t dtype = DDP_FP32;
+  int32_t dtype = DDP_FP32;             // the gradients' dtype (arena layout)
+  int32_t comm_dtype = DDP_FP32;        // the buckets' dtype (bucket layout, ring)
   int32_t world_size = 1;
   int64_t cap_bytes = 0;
   int64_t first_bucket_bytes = 0;
@@ -78,18 +79,19 @@ struct ddp_plan {
   std::vector<ddp::Bucket> buckets;
   std::vector<ddp::Segment> segments;   // all buckets' segments, bucket-major
   std::vector<ddp::Piece> pieces;       // all buckets' pieces, bucket-major
-  int64_t tile_elems = 0;               // elements per pack tile
+  int64_t tile_elems = 0;               // elements per pack tile (bucket vectors)
   std::mutex mu;                        // guards `device`
   ddp::DeviceTable device[ddp::kMaxDevices];
 };
 
 namespace ddp {
-// Elements covered by one pack/unpack tile; fixed when the plan is built so
-// the tile prefix sums in the segments match the kernels.
+// Elements covered by one pack/unpack tile, in vectors of the bucket's dtype
+// (16 bytes of it); fixed when the plan is built so the tile prefix sums in
+// the segments match the kernels.
 constexpr int kPackThreads = 256;
 constexpr int kPackVecsPerThread = 4;
-inline int64_t pack_tile_elems(int32_t dtype) {
-  return int64_t(kPackThreads) * kPackVecsPerThread * (kVectorBytes / elem_bytes(dtype));
+inline int64_t pack_tile_elems(int32_t comm_dtype) {
+  return int64_t(kPackThreads) * kPackVecsPerThread * (kVectorBytes / elem_bytes(comm_dtype));
 }
 // Elements covered by one tile of the in-place sync: one wave, one 16-byte
 // vector per thread.

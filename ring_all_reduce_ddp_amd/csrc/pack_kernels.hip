@@ -9,6 +9,11 @@
 // the world size and copied back. Here the division is a multiplication by
 // the caller's fp32 `scale` (1/N), fused into the copy back.
 //
+// A plan may keep fp32 gradients in bf16 buckets: the bf16 compression hook
+// (page "Day 17 数据并行 DP/DDP", reading list, "PyTorch DDP Communication
+// Hooks"). Packing then rounds each gradient to bf16, the ring runs in bf16,
+// and the copy back widens to fp32 and rounds the scaled value once.
+//
 // A bucket is a list of segments (each member's slot, then the zero padding);
 // each segment is covered by whole tiles so a block never mixes segments, and
 // a block finds its segment by a uniform binary search over the tile prefix
@@ -87,6 +92,73 @@ __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, 
   }
 }
 
+// fp32 gradients into a bf16 bucket (the bf16 compression hook): every
+// gradient is rounded to the nearest bf16, ties to even. A bucket vector is 8
+// bf16 elements; it reads two 16-byte vectors of fp32 gradients.
+__global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* segs, int n_segs, int64_t n_tiles,
+                                                               RankPtrs arenas, RankPtrs buckets) {
+  constexpr int V = 8;
+  constexpr int U = kPackVecsPerThread;
+  constexpr int64_t kTile = int64_t(kThreads) * U * V;
+  const float* arena = static_cast<const float*>(arenas.p[blockIdx.y]);
+  void* bucket = buckets.p[blockIdx.y];
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const int64_t first = (tile - sg.tile_begin) * kTile;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e >= sg.slot) continue;
+      u32x4* d = static_cast<u32x4*>(bucket) + (sg.dst_off + e) / V;
+      if (e + V <= sg.numel) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(arena + sg.src_off + e);
+        const u32x4 a = src[0], b = src[1];
+        *d = u32x4{bf16_pack(round_bf16(__uint_as_float(a.x)), round_bf16(__uint_as_float(a.y))),
+                   bf16_pack(round_bf16(__uint_as_float(a.z)), round_bf16(__uint_as_float(a.w))),
+                   bf16_pack(round_bf16(__uint_as_float(b.x)), round_bf16(__uint_as_float(b.y))),
+                   bf16_pack(round_bf16(__uint_as_float(b.z)), round_bf16(__uint_as_float(b.w)))};
+      } else if (e >= sg.numel) {
+        *d = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        for (int i = 0; i < V; ++i)
+          Ops<DDP_BF16>::store1(bucket, sg.dst_off + e + i,
+                                e + i < sg.numel ? round_bf16(arena[sg.src_off + e + i]) : 0.0f);
+      }
+    }
+  }
+}
+
+// bf16 bucket back into fp32 gradients: each bf16 value (exact in fp32) is
+// multiplied by `scale` and rounded once to fp32.
+__global__ __launch_bounds__(kThreads) void k_unpack_bf16_to_f32(const Segment* segs, int n_segs, int64_t n_tiles,
+                                                                 RankPtrs buckets, RankPtrs arenas, float scale) {
+  constexpr int V = 8;
+  constexpr int U = kPackVecsPerThread;
+  constexpr int64_t kTile = int64_t(kThreads) * U * V;
+  const void* bucket = buckets.p[blockIdx.y];
+  float* arena = static_cast<float*>(arenas.p[blockIdx.y]);
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const int64_t first = (tile - sg.tile_begin) * kTile;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e >= sg.numel) continue;
+      if (e + V <= sg.numel) {
+        const u32x4 x = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
+        u32x4* dst = reinterpret_cast<u32x4*>(arena + sg.src_off + e);
+        dst[0] = u32x4{__float_as_uint(bf16_lo(x.x) * scale), __float_as_uint(bf16_hi(x.x) * scale),
+                       __float_as_uint(bf16_lo(x.y) * scale), __float_as_uint(bf16_hi(x.y) * scale)};
+        dst[1] = u32x4{__float_as_uint(bf16_lo(x.z) * scale), __float_as_uint(bf16_hi(x.z) * scale),
+                       __float_as_uint(bf16_lo(x.w) * scale), __float_as_uint(bf16_hi(x.w) * scale)};
+      } else {
+        for (int64_t i = e; i < sg.numel; ++i)
+          arena[sg.src_off + i] = Ops<DDP_BF16>::load1(bucket, sg.dst_off + i) * scale;
+      }
+    }
+  }
+}
+
 bool spans_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return abytes > 0 && bbytes > 0 && x < y + uint64_t(bbytes) && y < x + uint64_t(abytes);
@@ -100,9 +172,8 @@ int check_copy(const char* fn, const ddp_plan* plan, int32_t b, const void* cons
     return fail(DDP_EINVAL, std::string(fn) + ": bucket index out of range");
   if (N != plan->world_size)
     return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
-  const int eb = elem_bytes(plan->dtype);
-  const int64_t abytes = plan->arena_numel * eb;
-  const int64_t bbytes = plan->buckets[b].padded_numel * eb;
+  const int64_t abytes = plan->arena_numel * elem_bytes(plan->dtype);
+  const int64_t bbytes = plan->buckets[b].padded_numel * elem_bytes(plan->comm_dtype);
   int st = check_rank_buffers(const_cast<void* const*>(arenas), N, abytes, 16, fn, "grad_arenas");
   if (st != DDP_OK) return st;
   st = check_rank_buffers(const_cast<void* const*>(buckets), N, bbytes, 16, fn, "bucket_bufs");
@@ -181,7 +252,9 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   }
   const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
   hipStream_t s = as_stream(stream);
-  if (plan->dtype == DDP_FP32)
+  if (plan->dtype != plan->comm_dtype)
+    hipLaunchKernelGGL(k_pack_f32_to_bf16, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+  else if (plan->dtype == DDP_FP32)
     hipLaunchKernelGGL(k_pack<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
   else
     hipLaunchKernelGGL(k_pack<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
@@ -206,7 +279,10 @@ extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* 
   }
   const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
   hipStream_t s = as_stream(stream);
-  if (plan->dtype == DDP_FP32)
+  if (plan->dtype != plan->comm_dtype)
+    hipLaunchKernelGGL(k_unpack_bf16_to_f32, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, B,
+                       A, scale);
+  else if (plan->dtype == DDP_FP32)
     hipLaunchKernelGGL(k_unpack_scale<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs),
                        bk.n_tiles, B, A, scale);
   else
@@ -227,6 +303,8 @@ extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* co
     return fail(DDP_EINVAL, std::string(fn) + ": pointer array is NULL");
   if (N != plan->world_size) return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
   if (variant == DDP_VARIANT_VIEW) {
+    if (plan->comm_dtype != plan->dtype)
+      return fail(DDP_EINVAL, std::string(fn) + ": the in-place sync needs buckets of the gradients' dtype");
     for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
       int st = bucket_allreduce_view(plan, b, grad_arenas, N, scale, stream);
       if (st != DDP_OK) return st;
@@ -239,13 +317,13 @@ extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* co
     int st = bucket_pack(plan, b, const_cast<const void* const*>(grad_arenas), bufs, N, stream);
     if (st != DDP_OK) return st;
     if (variant == DDP_VARIANT_FUSED) {
-      st = ring_allreduce_fused(bufs, N, count, plan->dtype, stream);
+      st = ring_allreduce_fused(bufs, N, count, plan->comm_dtype, stream);
     } else if (variant == DDP_VARIANT_PERSISTENT) {
-      st = ring_allreduce_persistent(bufs, N, count, plan->dtype, 2 * (N - 1), stream);
+      st = ring_allreduce_persistent(bufs, N, count, plan->comm_dtype, 2 * (N - 1), stream);
     } else {
       for (int ph = DDP_RS; ph <= DDP_AG && st == DDP_OK; ++ph)
         for (int s = 0; s + 1 < N && st == DDP_OK; ++s)
-          st = ring_allreduce_step(bufs, N, count, plan->dtype, s, ph, stream);
+          st = ring_allreduce_step(bufs, N, count, plan->comm_dtype, s, ph, stream);
     }
     if (st != DDP_OK) return st;
     st = bucket_unpack_scale(plan, b, const_cast<const void* const*>(bufs), grad_arenas, N, scale, stream);

@@ -38,18 +38,33 @@ extern "C" const char* ddp_last_error(void) { return ddp::last_error(); }
 extern "C" int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, int32_t dtype,
                                int64_t cap_bytes, int64_t first_bucket_bytes,
                                int32_t world_size, ddp_plan** out) {
+  return ddp_bucket_plan_ex(param_numels, n_params, dtype, dtype, cap_bytes, first_bucket_bytes, world_size,
+                            out);
+}
+
+// grad_dtype: the gradients (arena layout; capacities count their bytes).
+// comm_dtype: the buckets (member alignment and padding in its 16-byte
+// vectors). fp32 gradients with bf16 buckets is the bf16 compression hook.
+extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params, int32_t grad_dtype,
+                                  int32_t comm_dtype, int64_t cap_bytes, int64_t first_bucket_bytes,
+                                  int32_t world_size, ddp_plan** out) {
+  const int32_t dtype = grad_dtype;
   if (out == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out is NULL");
   *out = nullptr;
   if (n_params < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: n_params < 0");
   if (n_params > 0 && param_numels == nullptr)
     return fail(DDP_EINVAL, "ddp_bucket_plan: param_numels is NULL");
-  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, "ddp_bucket_plan: unknown dtype");
+  if (!valid_dtype(grad_dtype) || !valid_dtype(comm_dtype))
+    return fail(DDP_EINVAL, "ddp_bucket_plan: unknown dtype");
+  if (grad_dtype != comm_dtype && !(grad_dtype == DDP_FP32 && comm_dtype == DDP_BF16))
+    return fail(DDP_EINVAL, "ddp_bucket_plan: the only mixed pair is fp32 gradients in bf16 buckets");
   if (cap_bytes <= 0 || first_bucket_bytes <= 0)
     return fail(DDP_EINVAL, "ddp_bucket_plan: capacities must be positive");
   if (world_size < 1 || world_size > DDP_MAX_RANKS)
     return fail(DDP_EINVAL, "ddp_bucket_plan: world_size must lie in [1, 64]");
-  const int64_t e = elem_bytes(dtype);
-  const int64_t v = kVectorBytes / e;
+  const int64_t e = elem_bytes(grad_dtype);                 // capacity unit
+  const int64_t va = kVectorBytes / e;                       // arena alignment
+  const int64_t v = kVectorBytes / elem_bytes(comm_dtype);   // bucket alignment
   // Keep every size well inside int64 when multiplied by element sizes.
   const int64_t kMaxNumel = int64_t(1) << 50;
   for (int32_t p = 0; p < n_params; ++p) {
@@ -61,19 +76,20 @@ extern "C" int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, in
   ddp_plan* plan = new (std::nothrow) ddp_plan();
   if (plan == nullptr) return fail(DDP_ENOMEM, "ddp_bucket_plan: out of host memory");
   try {
-    plan->dtype = dtype;
+    plan->dtype = grad_dtype;
+    plan->comm_dtype = comm_dtype;
     plan->world_size = world_size;
     plan->cap_bytes = cap_bytes;
     plan->first_bucket_bytes = first_bucket_bytes;
     plan->numels.assign(param_numels, param_numels + n_params);
-    plan->tile_elems = pack_tile_elems(dtype);
+    plan->tile_elems = pack_tile_elems(comm_dtype);
 
     // Gradient arena: registration order, each parameter on a 16-byte boundary.
     plan->arena_offsets.resize(n_params);
     int64_t pos = 0;
     for (int32_t p = 0; p < n_params; ++p) {
       plan->arena_offsets[p] = pos;
-      pos += round_up(param_numels[p], v);
+      pos += round_up(param_numels[p], va);
     }
     plan->arena_numel = pos;
 
@@ -124,14 +140,16 @@ extern "C" int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, in
       b.n_segs = int64_t(plan->segments.size()) - b.seg_begin;
       b.n_tiles = tiles;
 
-      // Pieces: each member cut at the bucket's ring-chunk boundaries
-      // (L = padded / N, a multiple of V), so a piece has one ring order.
+      // Pieces (for the in-place sync, same dtypes only): each member cut at
+      // the bucket's ring-chunk boundaries (L = padded / N, a multiple of V),
+      // so a piece has one ring order.
       b.piece_begin = int64_t(plan->pieces.size());
       const int64_t L = b.padded_numel / world_size;
       const int64_t vt = view_tile_elems(dtype);
       int64_t vtiles = 0;
       for (const Member& m : b.members) {
         b.data_numel += m.numel;
+        if (comm_dtype != grad_dtype) continue;
         for (int64_t pos = m.offset; pos < m.offset + m.numel;) {
           const int64_t c = pos / L;
           const int64_t end = std::min(m.offset + m.numel, (c + 1) * L);

@@ -129,6 +129,8 @@ extern "C" int bucket_allreduce_view(const ddp_plan* plan, int32_t b, void* cons
   if (b < 0 || b >= int32_t(plan->buckets.size()))
     return fail(DDP_EINVAL, std::string(fn) + ": bucket index out of range");
   if (N != plan->world_size) return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
+  if (plan->comm_dtype != plan->dtype)
+    return fail(DDP_EINVAL, std::string(fn) + ": the in-place sync needs buckets of the gradients' dtype");
   const int eb = elem_bytes(plan->dtype);
   int st = check_rank_buffers(grad_arenas, N, plan->arena_numel * eb, 16, fn, "grad_arenas");
   if (st != DDP_OK) return st;

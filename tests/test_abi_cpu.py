@@ -162,3 +162,30 @@ def test_reduce_scatter_argument_errors():
     odd = (ctypes.c_void_p * 2)(0x3001, 0x4000)
     # empty buffers: nothing to check or launch
     assert lib.ring_reduce_scatter_fused(bufs, odd, 2, 0, rar.DDP_FP32, 1.0, None) == rar.DDP_OK
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_compressed_plan_matches_oracle(seed):
+    """fp32 gradients in bf16 buckets: capacities count fp32 bytes, members and
+    padding use bf16 vectors (8 elements)."""
+    rng = np.random.default_rng(2000 + seed)
+    numels = [int(x) for x in rng.integers(0, 20000, size=rng.integers(1, 60))]
+    cap = int(rng.integers(16, 100000))
+    first = int(rng.integers(16, 100000))
+    n = int(rng.integers(1, 65))
+    p = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", cap, first, n)
+    want = planner.plan(numels, 4, cap, first, n, vector_elems=8)
+    assert p.buckets() == as_tuples(want)
+    arena_numel, offs = p.grad_arena()
+    assert all(o % 4 == 0 for o in offs)
+
+
+def test_compressed_plan_errors():
+    lib = rar.lib
+    out = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 1)(4)
+    expect_status(lib.ddp_bucket_plan_ex(arr, 1, rar.DDP_BF16, rar.DDP_FP32, 1024, 1024, 1, ctypes.byref(out)),
+                  rar.DDP_EINVAL, "mixed pair")
+    p = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
+    bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    expect_status(lib.bucket_allreduce_view(p.handle, 0, bufs, 2, 0.5, None), rar.DDP_EINVAL, "gradients' dtype")

@@ -167,3 +167,50 @@ def test_resnet50_sync(resnet50_case, variant):
     for r in range(w.n):
         for p in range(len(numels)):
             assert_bit_equal(got[r][p], want[r][p], f"{variant} rank {r} param {p}")
+
+
+@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_bf16_compressed_sync(variant, n):
+    """fp32 gradients synced through bf16 buckets (the bf16 compression hook)
+    equal the oracle's compressed sync bit for bit."""
+    numels = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5]
+    cap, first = 64 * 1024, 512
+    plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", cap, first, n)
+    grads = host_grads(60 + n, n, numels)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, n, "bf16")
+    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+    torch.cuda.synchronize()
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+    got = read_grads(arenas, offs, numels, "fp32")
+    oplan = planner.plan(numels, 4, cap, first, n, vector_elems=8)
+    want = ddp.ddp_sync(grads, oplan, "fp32", comm_dtype="bf16")
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{variant} n={n} rank {r} param {p}")
+
+
+def test_bf16_compressed_resnet50():
+    w = WORKLOADS["ddp_resnet50"]
+    numels = resnet50_param_numels()
+    grads = host_grads(w.seed, w.n, numels, std=w.std)
+    plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=w.n)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, w.n, "bf16")
+    rar.ddp_sync(plan, arenas, buckets, variant="fused", scale=0.125)
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, "fp32")
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, world_size=w.n, vector_elems=8), "fp32",
+                        scale=0.125, comm_dtype="bf16")
+    for r in range(w.n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"rank {r} param {p}")
+
+
+def test_view_refuses_compressed_plan():
+    plan = rar.ddp_bucket_plan_ex([100, 200], "fp32", "bf16", world_size=2)
+    arenas, _ = make_arenas(plan, host_grads(1, 2, [100, 200]), "fp32")
+    with pytest.raises(rar.DDPError, match="gradients' dtype"):
+        rar.ddp_sync(plan, arenas, None, variant="view")
