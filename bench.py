@@ -9,9 +9,10 @@ all-reduce), algorithm bandwidth S / t, and the HBM bandwidth of the kernel,
 
 Beside it, in the same run: the step-by-step and persistent forms, the
 reduce-scatter output alone, and the bf16 buffers of the same workload, a
-copy probe, the whole DDP sync of
-ResNet-50 gradients (8 ranks), the 64-rank 300M-element workload, and the CPU
-oracle timed on the headline workload's own inputs.
+copy probe, the whole DDP sync of ResNet-50 gradients (8 ranks; copying,
+in-place and bf16-compressed), the overlap of that sync with a synthetic
+backward over bucket capacities, the 64-rank 300M-element workload, and the
+CPU oracle timed on the headline workload's own inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
@@ -204,7 +205,48 @@ def main():
     sync["bf16_compressed_fused"] = {"ms": round(t, 4),
                                      "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
     extras["ddp_sync_resnet50_n8"] = sync
-    del arenas, buckets, cbuckets
+    del buckets, cbuckets
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ overlap with a synthetic backward
+    # Gradients are produced parameter by parameter in reverse order on one
+    # stream (each element copied after `work` dependent FMAs); the reducer
+    # syncs each bucket in place on another stream once its last gradient is
+    # ready. Swept over bucket capacities, as the pages' tuning experiment.
+    print("bench: overlap study", file=sys.stderr, flush=True)
+    srcs = [a.clone() for a in arenas]
+    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    overlap = {"sync": "in place (view)", "params": len(numels), "caps": {}}
+    for model, work, lds_kib in (("full_occupancy", 512, 0), ("two_waves_per_simd", 512, 64)):
+        rows = {}
+        for cap_name, cap, first in (("per_gradient", 1, 1), ("6MiB", 6 << 20, 1 << 20), ("12MiB", 12 << 20, 1 << 20),
+                                     ("25MiB", 25 << 20, 1 << 20), ("50MiB", 50 << 20, 1 << 20)):
+            cplan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=cap, first_bucket_bytes=first, world_size=wr.n)
+            red = rar.Reducer(cplan, arenas, None, variant="view", comm_stream=comm)
+
+            def backward(mode):
+                rar.ddp_synthetic_backward_pass(cplan, srcs, arenas, work,
+                                                red if mode == "overlapped" else None, lds_kib=lds_kib,
+                                                stream=compute)
+                if mode == "sequential":
+                    rar.ddp_sync(cplan, arenas, None, variant="view", stream=compute)
+
+            with torch.cuda.stream(compute):
+                res = {}
+                for mode in ("backward_only", "sequential", "overlapped"):
+                    backward(mode)
+                    res[mode] = time_launches(lambda: backward(mode), 3, torch)
+            red.free()
+            rows[cap_name] = {"buckets": cplan.num_buckets,
+                              "backward_only_ms": round(res["backward_only"], 4),
+                              "sequential_ms": round(res["sequential"], 4),
+                              "overlapped_ms": round(res["overlapped"], 4),
+                              "exposed_comm_ms": round(res["overlapped"] - res["backward_only"], 4),
+                              "overlap_gain": round(1 - res["overlapped"] / res["sequential"], 4)}
+        overlap["caps"][model] = rows
+        overlap["caps"][model]["backward_model"] = {"fma_per_element": work, "reserved_lds_kib_per_block": lds_kib}
+    extras["overlap_resnet50_n8"] = overlap
+    del arenas, srcs
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ 64 ranks x 300M fp32

@@ -269,6 +269,67 @@ int ring_reduce_scatter_fused(const void* const* bufs, void* const* shards, int3
 int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs,
              int32_t N, int32_t variant, float scale, void* stream);
 
+/* ---------------------------------------------------------------- overlap with backward
+ * The reducer launches each bucket's sync as soon as its last gradient is
+ * ready, on a communication stream, so that it overlaps the rest of backward
+ * ([R] section 03 "Overlap" and section 05 step 2: a hook per gradient; the
+ * last gradient of a bucket launches its all-reduce asynchronously; the same
+ * bucket order on every rank, bucket i+1 never before bucket i; [D]
+ * "梯度同步时机", "源码阅读路线"). One host thread drives a reducer.
+ *
+ * ddp_reducer_create: for `plan`, gradient arenas grad_arenas[N] and, unless
+ *   variant is DDP_VARIANT_VIEW, bucket buffers bucket_bufs[B*N] (layout as
+ *   for ddp_sync); each bucket's sync is the `variant` one with `scale`, and
+ *   runs on comm_stream. The pointer arrays are copied; the plan must outlive
+ *   the reducer. For DDP_VARIANT_VIEW the arenas are checked here, once, and
+ *   must stay allocated while the reducer exists.
+ *   comm_max_blocks (DDP_VARIANT_VIEW only; 0 for no limit): the syncs of all
+ *   buckets but the last run on at most this many one-wave blocks, so they
+ *   take few of the compute units that backward is still using (the way a
+ *   collective library limits the channels a collective occupies); the last
+ *   bucket, ready only once backward is over, runs full width. Results do not
+ *   depend on it.
+ *   The reducer starts prepared for a backward pass. */
+typedef struct ddp_reducer ddp_reducer;
+int ddp_reducer_create(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs, int32_t N,
+                       int32_t variant, float scale, int64_t comm_max_blocks, void* comm_stream,
+                       ddp_reducer** out);
+void ddp_reducer_free(ddp_reducer* reducer);
+/* Start of a backward pass: no gradient is ready. */
+int ddp_reducer_prepare(ddp_reducer* reducer);
+/* Gradient `param` (of every rank) has been produced by work already enqueued
+ * on producer_stream. If it completes its bucket, an event recorded on
+ * producer_stream gates that bucket's sync, which is enqueued on the
+ * communication stream once every earlier bucket has been. Marking a
+ * parameter twice in one pass is an error. */
+int ddp_reducer_mark_ready(ddp_reducer* reducer, int32_t param, void* producer_stream);
+/* End of backward: `stream` waits until every bucket's sync has finished.
+ * Returns DDP_EINVAL, naming the parameter, if some gradient was never marked
+ * ready (where DDP would wait for it forever). */
+int ddp_reducer_finalize(ddp_reducer* reducer, void* stream);
+
+/* ddp_synthetic_backward: a stand-in for the backward kernels that produce
+ * gradients, for overlap measurements: dsts[r][i] = srcs[r][i] for every rank
+ * r < N and i < numel, after `work` dependent fused multiply-adds per element
+ * that do not change the copied value. Each 256-thread block reserves
+ * lds_kib KiB of LDS (0..64) that it never uses, which caps how many blocks
+ * share a compute unit (64 KiB: two blocks, two waves per SIMD), the way
+ * register- or LDS-hungry backward kernels are capped. */
+int ddp_synthetic_backward(const void* const* srcs, void* const* dsts, int32_t N, int64_t numel, int32_t dtype,
+                           int32_t work, int32_t lds_kib, void* stream);
+
+/* ddp_synthetic_backward_pass: one synthetic backward pass over the plan's
+ * parameters in reverse registration order (the order DDP's bucketing
+ * assumes backward produces them, [R] section 03 "Overlap"): for every
+ * parameter p, ddp_synthetic_backward copies src_arenas[r]'s gradient p into
+ * grad_arenas[r] on `stream` for all N ranks (with `work` and lds_kib as
+ * there), then, if `reducer` is not NULL,
+ * marks p ready. With a reducer the pass starts with ddp_reducer_prepare and
+ * ends with ddp_reducer_finalize(stream). Arenas are laid out as for
+ * bucket_pack. */
+int ddp_synthetic_backward_pass(const ddp_plan* plan, const void* const* src_arenas, void* const* grad_arenas,
+                                int32_t N, int32_t work, int32_t lds_kib, ddp_reducer* reducer, void* stream);
+
 /* ---------------------------------------------------------------- checks and probes
  * ddp_count_mismatches: *out_dev (a device uint64, overwritten) receives the
  * number of element positions at which some rank's bits differ from rank 0's

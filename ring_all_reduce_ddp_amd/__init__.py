@@ -76,6 +76,13 @@ def _load():
         "bucket_allreduce_view": (ctypes.c_int, [vp, i32, pp, i32, f32, vp]),
         "ring_reduce_scatter_fused": (ctypes.c_int, [pp, pp, i32, i64, i32, f32, vp]),
         "ddp_sync": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, vp]),
+        "ddp_reducer_create": (ctypes.c_int, [vp, pp, pp, i32, i32, f32, i64, vp, ctypes.POINTER(vp)]),
+        "ddp_reducer_free": (None, [vp]),
+        "ddp_reducer_prepare": (ctypes.c_int, [vp]),
+        "ddp_reducer_mark_ready": (ctypes.c_int, [vp, i32, vp]),
+        "ddp_reducer_finalize": (ctypes.c_int, [vp, vp]),
+        "ddp_synthetic_backward": (ctypes.c_int, [pp, pp, i32, i64, i32, i32, i32, vp]),
+        "ddp_synthetic_backward_pass": (ctypes.c_int, [vp, pp, pp, i32, i32, i32, vp, vp]),
         "ddp_count_mismatches": (ctypes.c_int, [pp, i32, i64, i32, vp, vp]),
         "ddp_copy_probe": (ctypes.c_int, [vp, vp, i64, vp]),
     }
@@ -323,6 +330,64 @@ def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, s
         scale = 1.0 / n
     _check(_get_lib().ddp_sync(plan.handle, _ptr_array(grad_arenas), bufs, n, VARIANTS[variant], float(scale),
                         _stream(stream)))
+
+
+class Reducer:
+    """Launches each bucket's sync as soon as its last gradient is marked
+    ready, on `comm_stream` (see ddp_reducer_* in include/ddp_ring.h).
+    bucket_bufs: list over buckets of lists over ranks; None for "view"."""
+
+    def __init__(self, plan, grad_arenas, bucket_bufs=None, variant="view", scale=None, comm_stream=None,
+                 comm_max_blocks=0):
+        n = len(grad_arenas)
+        self.plan = plan   # the plan must outlive the reducer
+        if bucket_bufs is None:
+            bufs = None
+        else:
+            flat = [x for row in bucket_bufs for x in row] if isinstance(bucket_bufs[0], (list, tuple)) \
+                else list(bucket_bufs)
+            bufs = _ptr_array(flat)
+        h = ctypes.c_void_p()
+        _check(_get_lib().ddp_reducer_create(plan.handle, _ptr_array(grad_arenas), bufs, n, VARIANTS[variant],
+                                             float(1.0 / n if scale is None else scale), int(comm_max_blocks),
+                                             _stream(comm_stream), ctypes.byref(h)))
+        self._h = h.value
+
+    def prepare(self):
+        _check(_get_lib().ddp_reducer_prepare(self._h))
+
+    def mark_ready(self, param, stream=None):
+        _check(_get_lib().ddp_reducer_mark_ready(self._h, int(param), _stream(stream)))
+
+    def finalize(self, stream=None):
+        _check(_get_lib().ddp_reducer_finalize(self._h, _stream(stream)))
+
+    def free(self):
+        if self._h:
+            _get_lib().ddp_reducer_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def ddp_synthetic_backward(srcs, dsts, work, lds_kib=0, numel=None, dtype=None, stream=None):
+    """dsts[r][:numel] = srcs[r][:numel] after `work` FMAs per element (a
+    stand-in for the backward kernels that produce gradients)."""
+    ptrs, n, numel, dt = _ring_args(srcs, numel, dtype)
+    _check(_get_lib().ddp_synthetic_backward(ptrs, _ptr_array(dsts), n, numel, dt, int(work), int(lds_kib),
+                                             _stream(stream)))
+
+
+def ddp_synthetic_backward_pass(plan, src_arenas, grad_arenas, work, reducer=None, lds_kib=0, stream=None):
+    """One synthetic backward over the plan's parameters in reverse order,
+    marking each gradient ready on `reducer` (if given) as it is produced."""
+    _check(_get_lib().ddp_synthetic_backward_pass(plan.handle, _ptr_array(src_arenas), _ptr_array(grad_arenas),
+                                                  len(grad_arenas), int(work), int(lds_kib),
+                                                  None if reducer is None else reducer._h, _stream(stream)))
 
 
 def ddp_count_mismatches(bufs, out, count=None, dtype=None, stream=None):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libddp_ring.so")
 
-HIP_SOURCES = ["fused_kernels.hip", "ring_kernels.hip", "pack_kernels.hip", "view_kernels.hip", "scatter_kernels.hip", "runtime.hip"]
+HIP_SOURCES = ["fused_kernels.hip", "ring_kernels.hip", "pack_kernels.hip", "view_kernels.hip", "scatter_kernels.hip", "reducer.hip", "runtime.hip"]
 HOST_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

@@ -30,15 +30,14 @@ struct Segment {
   int64_t tile_begin;  // first pack tile of this segment (prefix sum)
 };
 
-// A run of one member's elements that lies inside one ring chunk of its
-// bucket: the unit of work of the in-place (bucket-view) sync.
-struct Piece {
-  int64_t src_off;     // offset in the gradient arena, elements (multiple of V)
-  int64_t numel;       // elements
-  int64_t tile_begin;  // first view tile of this piece (prefix sum)
-  int32_t chunk;       // ring chunk of the bucket that holds these elements
-  int32_t reserved;
-};
+// The in-place sync's map of the gradient arena: one entry per 16-byte
+// vector, kVecSlack for vectors that hold no member element (the padding
+// between members), else the ring chunk of the vector's bucket that holds it
+// (low byte) and how many of its elements belong to the member (high byte,
+// 1..V; fewer than V only for a member's last vector). A vector never spans
+// two chunks: chunk boundaries and member offsets are multiples of V.
+constexpr uint16_t kVecSlack = 0xffff;
+inline uint16_t make_vec_info(int64_t chunk, int64_t valid) { return uint16_t(chunk | (valid << 8)); }
 
 struct Member {
   int32_t param;
@@ -52,17 +51,17 @@ struct Bucket {
   int64_t seg_begin = 0;   // index of its first segment in plan.segments
   int64_t n_segs = 0;
   int64_t n_tiles = 0;     // pack/unpack tiles per rank
-  int64_t piece_begin = 0; // index of its first piece in plan.pieces
-  int64_t n_pieces = 0;
-  int64_t n_view_tiles = 0;
+  int64_t view_vec_begin = 0;  // the bucket's members span arena vectors
+  int64_t view_vec_end = 0;    // [view_vec_begin, view_vec_end) (in-place sync)
+  int64_t n_view_tiles = 0;    // view tiles covering that span
   int64_t data_numel = 0;  // sum of its members' element counts
 };
 
 constexpr int kMaxDevices = 64;
 
 struct DeviceTable {
-  Segment* segs = nullptr;   // device copy of plan.segments
-  Piece* pieces = nullptr;   // device copy of plan.pieces (same allocation)
+  Segment* segs = nullptr;       // device copy of plan.segments
+  uint16_t* vec_info = nullptr;  // device copy of plan.vec_info (same allocation)
 };
 
 }  // namespace ddp
@@ -78,7 +77,7 @@ struct ddp_plan {
   int64_t arena_numel = 0;
   std::vector<ddp::Bucket> buckets;
   std::vector<ddp::Segment> segments;   // all buckets' segments, bucket-major
-  std::vector<ddp::Piece> pieces;       // all buckets' pieces, bucket-major
+  std::vector<uint16_t> vec_info;       // per arena vector (in-place sync; same dtypes only)
   int64_t tile_elems = 0;               // elements per pack tile (bucket vectors)
   std::mutex mu;                        // guards `device`
   ddp::DeviceTable device[ddp::kMaxDevices];
@@ -93,15 +92,11 @@ constexpr int kPackVecsPerThread = 4;
 inline int64_t pack_tile_elems(int32_t comm_dtype) {
   return int64_t(kPackThreads) * kPackVecsPerThread * (kVectorBytes / elem_bytes(comm_dtype));
 }
-// Elements covered by one tile of the in-place sync: one wave, one 16-byte
-// vector per thread.
+// Arena vectors covered by one tile of the in-place sync (one per lane of a wave).
 constexpr int kViewThreads = 64;
-inline int64_t view_tile_elems(int32_t dtype) {
-  return int64_t(kViewThreads) * (kVectorBytes / elem_bytes(dtype));
-}
-// Device copies of the plan's segment and piece tables on the current
-// device, made on first use (defined with the HIP code).
-int device_tables(ddp_plan* plan, const Segment** segs, const Piece** pieces);
+// Device copies of the plan's segment table and arena vector map on the
+// current device, made on first use (defined with the HIP code).
+int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info);
 // Releases the device tables of a plan (defined with the HIP code).
 void release_device_tables(ddp_plan* plan);
 }  // namespace ddp

@@ -16,110 +16,100 @@ namespace {
 
 // ---------------------------------------------------------------- fused
 //
-// Launch shape, measured on MI355X at 8 ranks x 1 GiB: one wave (64 threads)
-// per block, one 16-byte vector per thread per rank, one tile per block, and
-// non-temporal stores (the result is not read again by this kernel).
-// Single-wave blocks retire independently, which kept the memory system
-// busier than 256-thread blocks (5.86 vs 5.50 TB/s for fp32); grid-stride
-// loops over a resident grid were slower still. Loads are non-temporal when
-// the N buffers together exceed the 256 MB Infinity Cache; when they fit
-// (a DDP bucket: 8 x 25 MiB) cached loads find data written just before
-// (7.05 vs 6.65 TB/s). Tiles are numbered either chunk-major (tile t of
-// chunk c is block c * tiles_per_chunk + t) or interleaved across chunks
-// (block t * N + c); fp32 ran faster interleaved and bf16 chunk-major.
+// Launch shape, measured on MI355X at 8 ranks x 1 GiB fp32. A tile is 64
+// vectors of 16 bytes of one chunk, on a grid aligned to whole tiles, and a
+// block has one wave per rank (N <= 8; above that eight waves, each taking
+// every eighth rank). Wave w loads rank w's tile into LDS row w, the block
+// sums each 32-bit word down the rows in ring order, and wave w stores the
+// result to rank w: every wave streams one rank's buffer, one load and one
+// store per lane. That ran at 6.1-6.2 TB/s, where one-wave blocks that each
+// read all N ranks and write all N ranks reached 5.7-5.8 TB/s on the same
+// parts; the staged form also leaves far more room to a compute kernel
+// running beside it on another stream. Tiles go chunk by chunk (chunk-major
+// and chunk-interleaved orders ran alike at 1 GiB, chunk-major faster at
+// 24 MiB per rank). Stores are non-temporal (the result is not read again
+// here); loads are too when the N buffers together exceed the 256 MB
+// Infinity Cache, and cached when they fit (a DDP bucket: 8 x 25 MiB), so
+// they find data written just before.
 
-constexpr int kFusedThreads = 64;
+constexpr int kFusedThreads = 64;   // threads per wave and vectors per rank tile
+constexpr int kFusedMaxWaves = 8;
 constexpr int64_t kFusedCacheResidentBytes = int64_t(256) << 20;
-constexpr int kFusedBatch = 16;   // ranks loaded together by the any-N kernel
 
-template <int DT>
-struct FusedOrder {
-  static constexpr bool interleave = DT == DDP_FP32;
-};
-
-__device__ __forceinline__ void fused_tile(int64_t tile, int n, int64_t tiles_per_chunk, bool interleave,
-                                           int* c, int64_t* t) {
-  if (interleave) {
-    *c = int(tile % n);
-    *t = tile / n;
+// LDS for one tile of every rank: a fixed array for a compile-time rank
+// count, else the launch's dynamic LDS (N KiB).
+template <int NR>
+__device__ __forceinline__ u32x4* staged_tile() {
+  if constexpr (NR > 0) {
+    __shared__ u32x4 tile[NR * kFusedThreads];
+    return tile;
   } else {
-    *c = int(tile / tiles_per_chunk);
-    *t = tile - int64_t(*c) * tiles_per_chunk;
+    extern __shared__ u32x4 dyn[];
+    return dyn;
   }
 }
 
+// NR > 0: compile-time rank count and NR waves; NR == 0: any N, kFusedMaxWaves
+// waves, each taking every kFusedMaxWaves-th rank. LDS: N rows of one tile
+// (N KiB); the sum overwrites row 0 word by word (each word is read and
+// written by one thread only). Grid: (tiles of a chunk from tile t0 on, N
+// chunks); each block does one tile, so it knows its chunk without a
+// division, blocks run chunk by chunk, and nothing loops (a grid-stride
+// form of the same kernel, with a barrier before each refill of the stage,
+// ran ~6 % slower).
 template <int DT, int NR, bool NTL>
-__global__ __launch_bounds__(kFusedThreads) void k_fused_vec(RankPtrs P, int64_t count, int64_t L,
-                                                             int64_t tiles_per_chunk, int64_t total_tiles) {
+__global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_staged(RankPtrs P, int n_rt, int64_t count,
+                                                                               int64_t L, int64_t t0) {
   using O = Ops<DT>;
+  using Wd = Word<DT>;
   constexpr int V = O::V;
-  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    int c;
-    int64_t t;
-    fused_tile(tile, NR, tiles_per_chunk, FusedOrder<DT>::interleave, &c, &t);
-    const int64_t lo = int64_t(c) * L;
-    const int64_t hi = min(lo + L, count);
-    const int64_t vi = tile_vector(lo, t, kFusedThreads, V);
-    if (vi * V < lo || vi * V >= hi) continue;
-    // Ring order of chunk c: rank c+1 first, then c+2, ..., c.
-    const void* src[NR];
+  constexpr int W = NR > 0 ? NR : kFusedMaxWaves;
+  constexpr int kSlots = NR > 0 ? 1 : DDP_MAX_RANKS / kFusedMaxWaves;  // ranks per wave, at most
+  constexpr int kWords = kFusedThreads * 4;  // 32-bit words per rank tile
+  constexpr int64_t kTile = int64_t(kFusedThreads) * V;
+  u32x4* stage = staged_tile<NR>();
+  const int n = NR > 0 ? NR : n_rt;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kFusedThreads);
+  const int lane = int(threadIdx.x) % kFusedThreads;
+  const int c = int(blockIdx.y);
+  const int64_t lo = int64_t(c) * L;
+  const int64_t hi = min(lo + L, count);
+  const int64_t vi = (lo / kTile + t0 + blockIdx.x) * kFusedThreads + lane;
+  const int64_t e0 = vi * V;
+  const bool mine = e0 >= lo && e0 < hi;
+  const bool full = e0 + V <= hi;
+  if (mine) {
 #pragma unroll
-    for (int k = 0; k < NR; ++k) src[k] = P.p[wrap(c + 1 + k, NR)];
-    if ((vi + 1) * V <= hi) {
-      u32x4 x[NR];
-#pragma unroll
-      for (int k = 0; k < NR; ++k) x[k] = ld16<NTL>(static_cast<const u32x4*>(src[k]) + vi);
-      typename O::Acc a = O::from(x[0]);
-#pragma unroll
-      for (int k = 1; k < NR; ++k) O::add(a, x[k]);
-      const u32x4 y = O::to(a);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) st16<true>(static_cast<u32x4*>(P.p[r]) + vi, y);
-    } else {
-      // Ragged end of the buffer: the elements of this vector below `hi`.
-      for (int64_t e = vi * V; e < hi; ++e) {
-        float acc = O::load1(src[0], e);
-        for (int k = 1; k < NR; ++k) acc = O::add1(acc, O::load1(src[k], e));
-        for (int r = 0; r < NR; ++r) O::store1(P.p[r], e, acc);
+    for (int j = 0; j < kSlots; ++j) {
+      const int r = wave + j * W;
+      if (r < n) {
+        const u32x4* src = static_cast<const u32x4*>(P.p[r]);
+        stage[r * kFusedThreads + lane] = full ? ld16<NTL>(src + vi) : Wd::load_partial(src, e0, int(hi - e0));
       }
     }
   }
-}
-
-template <int DT, bool NTL>
-__global__ __launch_bounds__(kFusedThreads) void k_fused_vec_n(RankPtrs P, int n, int64_t count, int64_t L,
-                                                               int64_t tiles_per_chunk, int64_t total_tiles) {
-  using O = Ops<DT>;
-  constexpr int V = O::V;
-  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    int c;
-    int64_t t;
-    fused_tile(tile, n, tiles_per_chunk, FusedOrder<DT>::interleave, &c, &t);
-    const int64_t lo = int64_t(c) * L;
-    const int64_t hi = min(lo + L, count);
-    const int64_t vi = tile_vector(lo, t, kFusedThreads, V);
-    if (vi * V < lo || vi * V >= hi) continue;
-    const int first = wrap(c + 1, n);
-    if ((vi + 1) * V <= hi) {
-      typename O::Acc a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
-      // Ranks c+2, ..., c in order, loaded kFusedBatch at a time.
-      for (int k = 1; k < n; k += kFusedBatch) {
-        u32x4 x[kFusedBatch];
+  __syncthreads();
+  // Ring order of chunk c: rank c+1 first, then c+2, ..., c.
+  const int first = wrap(c + 1, n);
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(stage);
+  uint32_t* result = reinterpret_cast<uint32_t*>(stage);
+  for (int d = threadIdx.x; d < kWords; d += W * kFusedThreads) {
+    typename Wd::Acc a = Wd::from(words[first * kWords + d]);
+    for (int k = 1; k < n; ++k) Wd::add(a, words[wrap(first + k, n) * kWords + d]);
+    result[d] = Wd::out(a);
+  }
+  __syncthreads();
+  if (!mine) return;
+  const u32x4 y = stage[lane];
 #pragma unroll
-        for (int j = 0; j < kFusedBatch; ++j)
-          if (k + j < n) x[j] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
-#pragma unroll
-        for (int j = 0; j < kFusedBatch; ++j)
-          if (k + j < n) O::add(a, x[j]);
-      }
-      const u32x4 y = O::to(a);
-      for (int r = 0; r < n; ++r) st16<true>(static_cast<u32x4*>(P.p[r]) + vi, y);
+  for (int j = 0; j < kSlots; ++j) {
+    const int r = wave + j * W;
+    if (r >= n) continue;
+    if (full) {
+      st16<true>(static_cast<u32x4*>(P.p[r]) + vi, y);
     } else {
-      for (int64_t e = vi * V; e < hi; ++e) {
-        float acc = O::load1(P.p[first], e);
-        for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
-        for (int r = 0; r < n; ++r) O::store1(P.p[r], e, acc);
-      }
+      // Ragged end of the buffer: the elements of this vector below `hi`.
+      for (int i = 0; i < int(hi - e0); ++i) O::store1(P.p[r], e0 + i, Wd::elem(y, i));
     }
   }
 }
@@ -148,23 +138,27 @@ template <int DT, bool NTL>
 void launch_fused_vec(const RingArgs& a, hipStream_t s) {
   constexpr int V = Ops<DT>::V;
   const int64_t tpc = aligned_tiles_per_chunk(a.L, int64_t(kFusedThreads) * V);
-  const int64_t total = tpc * a.n;
-  const dim3 g(grid_for(total)), b(kFusedThreads);
-  switch (a.n) {
-#define DDP_FUSED_CASE(NR)                                                                      \
-  case NR:                                                                                      \
-    hipLaunchKernelGGL((k_fused_vec<DT, NR, NTL>), g, b, 0, s, a.P, a.count, a.L, tpc, total);  \
+  // One block per tile; chunks longer than kMaxGrid tiles take several launches.
+  for (int64_t t0 = 0; t0 < tpc; t0 += kMaxGrid) {
+    const dim3 g(unsigned(std::min(tpc - t0, kMaxGrid)), unsigned(a.n));
+    switch (a.n) {
+#define DDP_FUSED_CASE(NR)                                                                                 \
+  case NR:                                                                                                 \
+    hipLaunchKernelGGL((k_fused_staged<DT, NR, NTL>), g, dim3(kFusedThreads * NR), 0, s, a.P, a.n, a.count, \
+                       a.L, t0);                                                                            \
     break;
-    DDP_FUSED_CASE(2)
-    DDP_FUSED_CASE(3)
-    DDP_FUSED_CASE(4)
-    DDP_FUSED_CASE(5)
-    DDP_FUSED_CASE(6)
-    DDP_FUSED_CASE(7)
-    DDP_FUSED_CASE(8)
+      DDP_FUSED_CASE(2)
+      DDP_FUSED_CASE(3)
+      DDP_FUSED_CASE(4)
+      DDP_FUSED_CASE(5)
+      DDP_FUSED_CASE(6)
+      DDP_FUSED_CASE(7)
+      DDP_FUSED_CASE(8)
 #undef DDP_FUSED_CASE
-    default:
-      hipLaunchKernelGGL((k_fused_vec_n<DT, NTL>), g, b, 0, s, a.P, a.n, a.count, a.L, tpc, total);
+      default:
+        hipLaunchKernelGGL((k_fused_staged<DT, 0, NTL>), g, dim3(kFusedThreads * kFusedMaxWaves),
+                           size_t(a.n) * kFusedThreads * sizeof(u32x4), s, a.P, a.n, a.count, a.L, t0);
+    }
   }
 }
 

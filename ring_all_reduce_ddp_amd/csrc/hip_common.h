@@ -49,6 +49,17 @@ bool all_aligned16(void* const* bufs, int32_t n);
 // on `stream` ahead of it; *status the device's sticky timeout word.
 int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status);
 
+// The in-place sync of bucket b on arenas already checked by
+// check_view_arenas, with at most max_blocks blocks (0: as many as tiles)
+// (view_kernels.hip).
+int launch_view_bucket(const ddp_plan* plan, int32_t b, const RankPtrs& P, int32_t N, float scale,
+                       int64_t max_blocks, hipStream_t s);
+int check_view_arenas(const ddp_plan* plan, void* const* grad_arenas, int32_t N, const char* fn);
+
+// The synthetic backward kernel on already-checked buffers (runtime.hip).
+int launch_synthetic_backward(const RankPtrs& S, const RankPtrs& D, int32_t N, int64_t numel, int32_t dtype,
+                              int32_t work, int32_t lds_kib, hipStream_t s);
+
 // ---------------------------------------------------------------- device helpers
 
 // Round an fp32 value to the nearest bf16 (ties to even) and return the bf16
@@ -147,6 +158,56 @@ struct Ops<DDP_BF16> {
   }
   static __device__ __forceinline__ float add1(float a, float b) { return round_bf16(a + b); }
   static __device__ __forceinline__ float mul1(float a, float s) { return round_bf16(a * s); }
+};
+
+// One 32-bit word of a staged tile (one fp32 element or two bf16 elements):
+// the ring-order sum of the ranks' words, one rounding per add, then scaled.
+template <int DT>
+struct Word;
+
+template <>
+struct Word<DDP_FP32> {
+  struct Acc {
+    float v;
+  };
+  static __device__ __forceinline__ Acc from(uint32_t w) { return Acc{__uint_as_float(w)}; }
+  static __device__ __forceinline__ void add(Acc& a, uint32_t w) { a.v += __uint_as_float(w); }
+  static __device__ __forceinline__ uint32_t out(const Acc& a) { return __float_as_uint(a.v); }
+  static __device__ __forceinline__ uint32_t out(const Acc& a, float s) { return __float_as_uint(a.v * s); }
+  // Element j of a 16-byte vector, as an fp32 value.
+  static __device__ __forceinline__ float elem(u32x4 y, int j) { return __uint_as_float(y[j]); }
+  // Elements [e0, e0 + cnt) of p (cnt < 4) as a vector, the rest zero.
+  static __device__ __forceinline__ u32x4 load_partial(const void* p, int64_t e0, int cnt) {
+    u32x4 y = {0u, 0u, 0u, 0u};
+    const uint32_t* q = static_cast<const uint32_t*>(p) + e0;
+    for (int j = 0; j < cnt; ++j) y[j] = q[j];
+    return y;
+  }
+};
+
+template <>
+struct Word<DDP_BF16> {
+  struct Acc {
+    float lo, hi;
+  };
+  static __device__ __forceinline__ Acc from(uint32_t w) { return Acc{bf16_lo(w), bf16_hi(w)}; }
+  static __device__ __forceinline__ void add(Acc& a, uint32_t w) {
+    a.lo = round_bf16(a.lo + bf16_lo(w));
+    a.hi = round_bf16(a.hi + bf16_hi(w));
+  }
+  static __device__ __forceinline__ uint32_t out(const Acc& a) { return bf16_pack(a.lo, a.hi); }
+  static __device__ __forceinline__ uint32_t out(const Acc& a, float s) {
+    return bf16_pack(round_bf16(a.lo * s), round_bf16(a.hi * s));
+  }
+  static __device__ __forceinline__ float elem(u32x4 y, int j) {
+    return (j & 1) ? bf16_hi(y[j >> 1]) : bf16_lo(y[j >> 1]);
+  }
+  static __device__ __forceinline__ u32x4 load_partial(const void* p, int64_t e0, int cnt) {
+    u32x4 y = {0u, 0u, 0u, 0u};
+    const uint16_t* q = static_cast<const uint16_t*>(p) + e0;
+    for (int j = 0; j < cnt; ++j) y[j >> 1] |= uint32_t(q[j]) << ((j & 1) * 16);
+    return y;
+  }
 };
 
 template <bool NT>

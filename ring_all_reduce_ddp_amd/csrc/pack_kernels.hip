@@ -190,33 +190,33 @@ unsigned copy_grid(int64_t tiles) { return unsigned(std::max<int64_t>(1, std::mi
 
 }  // namespace
 
-int device_tables(ddp_plan* plan, const Segment** segs, const Piece** pieces) {
+int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info) {
   int dev = 0;
   DDP_HIP_TRY(hipGetDevice(&dev), "plan tables: hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "plan tables: device index beyond 64");
   std::lock_guard<std::mutex> lock(plan->mu);
   DeviceTable& t = plan->device[dev];
-  const size_t seg_bytes = sizeof(Segment) * plan->segments.size();
-  const size_t piece_bytes = sizeof(Piece) * plan->pieces.size();
-  if (t.segs == nullptr && seg_bytes + piece_bytes > 0) {
+  const size_t seg_bytes = size_t(round_up(int64_t(sizeof(Segment) * plan->segments.size()), 256));
+  const size_t map_bytes = sizeof(uint16_t) * plan->vec_info.size();
+  if (t.segs == nullptr && seg_bytes + map_bytes > 0) {
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, seg_bytes + piece_bytes);
+    hipError_t e = hipMalloc(&p, seg_bytes + map_bytes);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return fail(DDP_ENOMEM, std::string("plan tables: hipMalloc: ") + hipGetErrorString(e));
     }
-    e = hipMemcpy(p, plan->segments.data(), seg_bytes, hipMemcpyHostToDevice);
-    if (e == hipSuccess && piece_bytes > 0)
-      e = hipMemcpy(static_cast<char*>(p) + seg_bytes, plan->pieces.data(), piece_bytes, hipMemcpyHostToDevice);
+    e = hipMemcpy(p, plan->segments.data(), sizeof(Segment) * plan->segments.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && map_bytes > 0)
+      e = hipMemcpy(static_cast<char*>(p) + seg_bytes, plan->vec_info.data(), map_bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(p);
       return hip_fail(e, "plan tables: hipMemcpy");
     }
     t.segs = static_cast<Segment*>(p);
-    t.pieces = reinterpret_cast<Piece*>(static_cast<char*>(p) + seg_bytes);
+    t.vec_info = reinterpret_cast<uint16_t*>(static_cast<char*>(p) + seg_bytes);
   }
   if (segs) *segs = t.segs;
-  if (pieces) *pieces = t.pieces;
+  if (vec_info) *vec_info = t.vec_info;
   return DDP_OK;
 }
 
@@ -226,7 +226,7 @@ void release_device_tables(ddp_plan* plan) {
     if (t.segs != nullptr) {
       (void)hipFree(t.segs);
       t.segs = nullptr;
-      t.pieces = nullptr;
+      t.vec_info = nullptr;
     }
   }
 }

@@ -92,6 +92,7 @@ extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params,
       pos += round_up(param_numels[p], va);
     }
     plan->arena_numel = pos;
+    if (comm_dtype == grad_dtype) plan->vec_info.assign(pos / va, kVecSlack);
 
     // Buckets: reverse registration order.
     Bucket open;
@@ -140,33 +141,22 @@ extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params,
       b.n_segs = int64_t(plan->segments.size()) - b.seg_begin;
       b.n_tiles = tiles;
 
-      // Pieces (for the in-place sync, same dtypes only): each member cut at
-      // the bucket's ring-chunk boundaries (L = padded / N, a multiple of V),
-      // so a piece has one ring order.
-      b.piece_begin = int64_t(plan->pieces.size());
-      const int64_t L = b.padded_numel / world_size;
-      const int64_t vt = view_tile_elems(dtype);
-      int64_t vtiles = 0;
-      for (const Member& m : b.members) {
-        b.data_numel += m.numel;
-        if (comm_dtype != grad_dtype) continue;
-        for (int64_t pos = m.offset; pos < m.offset + m.numel;) {
-          const int64_t c = pos / L;
-          const int64_t end = std::min(m.offset + m.numel, (c + 1) * L);
-          Piece pc;
-          pc.src_off = plan->arena_offsets[m.param] + (pos - m.offset);
-          pc.numel = end - pos;
-          pc.tile_begin = vtiles;
-          pc.chunk = int32_t(c);
-          pc.reserved = 0;
-          // tiles on a grid aligned to whole tiles of the arena
-          vtiles += (pc.src_off + pc.numel + vt - 1) / vt - pc.src_off / vt;
-          plan->pieces.push_back(pc);
-          pos = end;
+      for (const Member& m : b.members) b.data_numel += m.numel;
+      // The in-place sync (same dtypes only): the bucket's members are a run
+      // of consecutive parameters, so they span one stretch of the arena.
+      if (comm_dtype == grad_dtype && !b.members.empty()) {
+        const Member& last = b.members.back();    // lowest parameter index
+        const Member& first = b.members.front();  // highest
+        b.view_vec_begin = plan->arena_offsets[last.param] / va;
+        b.view_vec_end = (plan->arena_offsets[first.param] + round_up(first.numel, va)) / va;
+        b.n_view_tiles = (b.view_vec_end + kViewThreads - 1) / kViewThreads - b.view_vec_begin / kViewThreads;
+        const int64_t L = b.padded_numel / world_size;
+        for (const Member& m : b.members) {
+          const int64_t a0 = plan->arena_offsets[m.param];
+          for (int64_t e = 0; e < m.numel; e += va)
+            plan->vec_info[(a0 + e) / va] = make_vec_info((m.offset + e) / L, std::min<int64_t>(va, m.numel - e));
         }
       }
-      b.n_pieces = int64_t(plan->pieces.size()) - b.piece_begin;
-      b.n_view_tiles = vtiles;
     }
   } catch (const std::bad_alloc&) {
     delete plan;

@@ -180,11 +180,79 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy16(u32x4* __restrict__ dst
     st16<true>(dst + i, ld16<true>(src + i));
 }
 
+// ---------------------------------------------------------------- synthetic backward
+
+// Stands in for the backward computation that produces a gradient: dst = src,
+// after `work` dependent fused multiply-adds per element on a separate
+// accumulator. The accumulator converges to 1 and never becomes NaN for
+// finite inputs, so the branch that would store it is never taken; the
+// compiler cannot know that, so the arithmetic is kept. The launch may
+// reserve dynamic LDS it never touches, to hold the kernel to a chosen
+// occupancy (as register- or LDS-hungry backward kernels are held).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_synthetic_backward(RankPtrs src, RankPtrs dst, int64_t numel,
+                                                                 int work) {
+  using O = Ops<DT>;
+  const void* s = src.p[blockIdx.y];
+  void* d = dst.p[blockIdx.y];
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  float x = i < numel ? O::load1(s, i) : 0.0f;
+  for (; i < numel; i += stride) {
+    // The next element's load is issued before this element's arithmetic,
+    // as compute-bound kernels hide their operand fetches.
+    // (The last iteration reloads its own element: an unconditional load
+    // lets the wait for it sit after the arithmetic.)
+    const float next = O::load1(s, min(i + stride, numel - 1));
+    float acc = x;
+    for (int k = 0; k < work; ++k) acc = __builtin_fmaf(acc, 0.999f, 0.001f);
+    O::store1(d, i, acc != acc ? acc : x);
+    x = next;
+  }
+}
+
 }  // namespace
 
 }  // namespace ddp
 
 using namespace ddp;
+
+namespace ddp {
+// Launches the synthetic backward on already-checked buffers.
+int launch_synthetic_backward(const RankPtrs& S, const RankPtrs& D, int32_t N, int64_t numel, int32_t dtype,
+                              int32_t work, int32_t lds_kib, hipStream_t s) {
+  if (numel == 0) return DDP_OK;
+  const int64_t blocks = std::min<int64_t>((numel + kThreads - 1) / kThreads, 4096);
+  const dim3 g(static_cast<unsigned>(blocks), static_cast<unsigned>(N));
+  const size_t lds = size_t(lds_kib) * 1024;
+  if (dtype == DDP_FP32)
+    hipLaunchKernelGGL(k_synthetic_backward<DDP_FP32>, g, dim3(kThreads), lds, s, S, D, numel, work);
+  else
+    hipLaunchKernelGGL(k_synthetic_backward<DDP_BF16>, g, dim3(kThreads), lds, s, S, D, numel, work);
+  DDP_HIP_TRY(hipGetLastError(), "ddp_synthetic_backward: launch");
+  return DDP_OK;
+}
+}  // namespace ddp
+
+extern "C" int ddp_synthetic_backward(const void* const* srcs, void* const* dsts, int32_t N, int64_t numel,
+                                      int32_t dtype, int32_t work, int32_t lds_kib, void* stream) {
+  const char* fn = "ddp_synthetic_backward";
+  if (!valid_dtype(dtype)) return fail(DDP_EINVAL, std::string(fn) + ": unknown dtype");
+  if (N < 1 || N > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
+  if (numel < 0 || work < 0) return fail(DDP_EINVAL, std::string(fn) + ": numel and work must be >= 0");
+  if (lds_kib < 0 || lds_kib > 64) return fail(DDP_EINVAL, std::string(fn) + ": lds_kib must lie in [0, 64]");
+  const int eb = elem_bytes(dtype);
+  int st = check_rank_buffers(const_cast<void* const*>(srcs), N, numel * eb, eb, fn, "srcs");
+  if (st != DDP_OK) return st;
+  st = check_rank_buffers(dsts, N, numel * eb, eb, fn, "dsts");
+  if (st != DDP_OK) return st;
+  RankPtrs S{}, D{};
+  for (int r = 0; r < N; ++r) {
+    S.p[r] = const_cast<void*>(srcs[r]);
+    D.p[r] = dsts[r];
+  }
+  return launch_synthetic_backward(S, D, N, numel, dtype, work, lds_kib, as_stream(stream));
+}
 
 extern "C" int ddp_persistent_status(void* stream) {
   DeviceScratch* s = nullptr;

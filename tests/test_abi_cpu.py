@@ -189,3 +189,21 @@ def test_compressed_plan_errors():
     p = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
     bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     expect_status(lib.bucket_allreduce_view(p.handle, 0, bufs, 2, 0.5, None), rar.DDP_EINVAL, "gradients' dtype")
+
+
+def test_reducer_argument_errors():
+    lib = rar.lib
+    out = ctypes.c_void_p()
+    bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    p = rar.ddp_bucket_plan([4, 8], "fp32", world_size=2)
+    expect_status(lib.ddp_reducer_create(None, bufs, None, 2, 3, 0.5, 0, None, ctypes.byref(out)), rar.DDP_EINVAL, "plan")
+    expect_status(lib.ddp_reducer_create(p.handle, bufs, None, 3, 3, 0.5, 0, None, ctypes.byref(out)), rar.DDP_EINVAL, "world size")
+    expect_status(lib.ddp_reducer_create(p.handle, bufs, None, 2, 0, 0.5, 0, None, ctypes.byref(out)), rar.DDP_EINVAL, "bucket_bufs")
+    expect_status(lib.ddp_reducer_create(p.handle, bufs, None, 2, 7, 0.5, 0, None, ctypes.byref(out)), rar.DDP_EINVAL, "variant")
+    expect_status(lib.ddp_reducer_create(p.handle, bufs, bufs, 2, 0, 0.5, 64, None, ctypes.byref(out)),
+                  rar.DDP_EINVAL, "in-place variant only")
+    expect_status(lib.ddp_reducer_create(p.handle, bufs, None, 2, 3, 0.5, -1, None, ctypes.byref(out)),
+                  rar.DDP_EINVAL, "comm_max_blocks < 0")
+    expect_status(lib.ddp_reducer_mark_ready(None, 0, None), rar.DDP_EINVAL, "NULL")
+    expect_status(lib.ddp_synthetic_backward(bufs, bufs, 2, 10, rar.DDP_FP32, -1, 0, None), rar.DDP_EINVAL, "work")
+    expect_status(lib.ddp_synthetic_backward(bufs, bufs, 2, 10, rar.DDP_FP32, 1, 65, None), rar.DDP_EINVAL, "lds_kib")

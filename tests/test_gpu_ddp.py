@@ -214,3 +214,36 @@ def test_view_refuses_compressed_plan():
     arenas, _ = make_arenas(plan, host_grads(1, 2, [100, 200]), "fp32")
     with pytest.raises(rar.DDPError, match="gradients' dtype"):
         rar.ddp_sync(plan, arenas, None, variant="view")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n", [4, 5, 7, 13, 64])
+def test_view_sync_more_ranks(dtype, n):
+    """The in-place sync at rank counts handled by each kernel form (one wave
+    per rank, and eight waves cycling over the ranks above eight, up to 64)."""
+    numels = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5]
+    sync_case("view", n, dtype, numels, 64 * 1024, 512, seed=140 + n)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_view_sync_leaves_slack_alone(dtype):
+    """The in-place sync writes the members' elements only: the arena's
+    alignment slack after each member keeps its bits."""
+    n = 3
+    numels = [5, 1, 30, 7, 1001, 3]
+    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=256, first_bucket_bytes=64, world_size=n)
+    grads = host_grads(44, n, numels)
+    arenas, offs = make_arenas(plan, grads, dtype)
+    arena_numel = arenas[0].numel()
+    slack = np.ones(arena_numel, bool)
+    for p, m in enumerate(numels):
+        slack[offs[p]:offs[p] + m] = False
+    assert slack.any()
+    idx = torch.from_numpy(np.nonzero(slack)[0]).cuda()
+    for a in arenas:
+        a.index_fill_(0, idx, 12345.0)
+    before = [to_host(a, dtype)[slack] for a in arenas]
+    rar.ddp_sync(plan, arenas, None, variant="view")
+    torch.cuda.synchronize()
+    for r, a in enumerate(arenas):
+        assert_bit_equal(to_host(a, dtype)[slack], before[r], f"slack of rank {r}")

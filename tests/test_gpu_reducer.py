@@ -1,0 +1,139 @@
+"""GPU tests of the reducer (buckets launched as their gradients become
+ready, on a separate stream) and of the synthetic backward used to measure
+overlap: results equal the oracle's whole sync bit for bit, in any marking
+order; a gradient never marked ready is reported."""
+
+import numpy as np
+import pytest
+import torch
+
+import ring_all_reduce_ddp_amd as rar
+from oracle import ddp, planner
+from ddp_workloads import host_grads, resnet50_param_numels
+
+from gpu_util import assert_bit_equal
+from test_gpu_ddp import make_arenas, read_grads, bucket_buffers
+
+pytestmark = pytest.mark.gpu
+
+NUMELS = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5, 100000, 33]
+
+
+def setup(variant, n, numels=NUMELS, cap=64 * 1024, first=512, seed=70):
+    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+    grads = host_grads(seed, n, numels)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = None if variant == "view" else bucket_buffers(plan, n, "fp32")
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, cap, first, n), "fp32")
+    return plan, grads, arenas, offs, buckets, want
+
+
+def check(arenas, offs, numels, want, n, what):
+    got = read_grads(arenas, offs, numels, "fp32")
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{what} rank {r} param {p}")
+
+
+@pytest.mark.parametrize("variant", ["view", "fused", "steps", "persistent"])
+@pytest.mark.parametrize("order", ["reverse", "forward", "shuffled"])
+def test_reducer_matches_oracle(variant, order):
+    n = 4
+    plan, grads, arenas, offs, buckets, want = setup(variant, n)
+    comm = torch.cuda.Stream()
+    red = rar.Reducer(plan, arenas, buckets, variant=variant, comm_stream=comm)
+    params = list(range(len(NUMELS)))
+    if order == "reverse":
+        params.reverse()
+    elif order == "shuffled":
+        np.random.default_rng(3).shuffle(params)
+    for p in params:
+        red.mark_ready(p)
+    red.finalize()
+    torch.cuda.synchronize()
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+    check(arenas, offs, NUMELS, want, n, f"{variant}/{order}")
+
+
+def test_reducer_reports_a_missing_gradient_and_recovers():
+    n = 2
+    plan, grads, arenas, offs, buckets, want = setup("view", n)
+    red = rar.Reducer(plan, arenas, variant="view", comm_stream=torch.cuda.Stream())
+    for p in range(len(NUMELS)):
+        if p != 6:
+            red.mark_ready(p)
+    with pytest.raises(rar.DDPError, match="parameter 6 was never marked ready"):
+        red.finalize()
+    with pytest.raises(rar.DDPError, match="twice"):
+        red.mark_ready(3)
+    torch.cuda.synchronize()
+    # a fresh pass over fresh gradients reduces everything
+    arenas2, _ = make_arenas(plan, grads, "fp32")
+    red2 = rar.Reducer(plan, arenas2, variant="view", comm_stream=torch.cuda.Stream())
+    red2.prepare()
+    for p in reversed(range(len(NUMELS))):
+        red2.mark_ready(p)
+    red2.finalize()
+    torch.cuda.synchronize()
+    check(arenas2, offs, NUMELS, want, n, "second pass")
+
+
+@pytest.mark.parametrize("variant", ["view", "fused"])
+def test_overlapped_backward_resnet50(variant):
+    """Synthetic backward (reverse parameter order) on one stream, buckets
+    reduced on another as they fill: the result equals the oracle's sync of
+    the same gradients, and equals a sequential run."""
+    n = 8
+    numels = resnet50_param_numels()
+    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=12 * 2 ** 20, world_size=n)
+    grads = host_grads(3, n, numels)
+    srcs, offs = make_arenas(plan, grads, "fp32")
+    arenas = [torch.full_like(s, float("nan")) for s in srcs]
+    buckets = None if variant == "view" else bucket_buffers(plan, n, "fp32")
+    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    red = rar.Reducer(plan, arenas, buckets, variant=variant, scale=0.125, comm_stream=comm)
+    with torch.cuda.stream(compute):
+        for p in reversed(range(len(numels))):
+            o, m = offs[p], numels[p]
+            rar.ddp_synthetic_backward([s[o:o + m] for s in srcs], [a[o:o + m] for a in arenas], work=16,
+                                       stream=compute)
+            red.mark_ready(p, stream=compute)
+        red.finalize(stream=compute)
+    torch.cuda.synchronize()
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, 12 * 2 ** 20, 2 ** 20, n), "fp32", scale=0.125)
+    check(arenas, offs, numels, want, n, f"overlapped {variant}")
+
+
+def test_synthetic_backward_copies_exactly():
+    src = [torch.randn(100003, device="cuda") for _ in range(3)]
+    src[0][5] = float("inf")
+    dst = [torch.empty_like(s) for s in src]
+    for lds in (0, 64):
+        rar.ddp_synthetic_backward(src, dst, work=100, lds_kib=lds)
+        torch.cuda.synchronize()
+        for s, d in zip(src, dst):
+            assert torch.equal(s, d)
+
+
+@pytest.mark.parametrize("cap_mib,blocks", [(1, 0), (25, 0), (25, 1), (6, 300)])
+def test_native_backward_pass_with_reducer(cap_mib, blocks):
+    """The library's own backward driver (reverse order, hook per gradient)
+    with the reducer gives the oracle's sync, whatever the width the syncs
+    run at during backward; without a reducer it only copies the gradients."""
+    n = 8
+    numels = resnet50_param_numels()
+    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=cap_mib << 20, world_size=n)
+    grads = host_grads(9, n, numels)
+    srcs, offs = make_arenas(plan, grads, "fp32")
+    arenas = [torch.full_like(s, float("nan")) for s in srcs]
+    rar.ddp_synthetic_backward_pass(plan, srcs, arenas, work=8)
+    torch.cuda.synchronize()
+    check(arenas, offs, numels, grads, n, "copy only")
+    comm = torch.cuda.Stream()
+    red = rar.Reducer(plan, arenas, variant="view", scale=0.125, comm_stream=comm, comm_max_blocks=blocks)
+    for _ in range(2):    # two passes: the reducer is re-armed by each pass
+        rar.ddp_synthetic_backward_pass(plan, srcs, arenas, work=8, reducer=red)
+    torch.cuda.synchronize()
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, cap_mib << 20, 2 ** 20, n), "fp32", scale=0.125)
+    check(arenas, offs, numels, want, n, f"pass with reducer, cap {cap_mib} MiB, {blocks} blocks")
