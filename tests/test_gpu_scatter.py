@@ -28,7 +28,8 @@ def shard_buffers(count, n, dtype):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("n,count", [(1, 100), (2, 4096), (3, 7), (5, 12345), (8, 8 * 2048 * 3),
-                                     (8, 8 * 4096 + 5), (8, 5), (9, 100_003), (16, 16 * 1000 + 8), (64, 64 * 1024)])
+                                     (8, 8 * 4096 + 5), (8, 5), (8, 25), (8, 7 * 4096 + 4093), (9, 100_003),
+                                     (16, 16 * 1000 + 8), (64, 64 * 1024)])
 @pytest.mark.parametrize("mean", [False, True])
 def test_shards_against_oracle(dtype, n, count, mean):
     host = host_ring_inputs(n * 7 + count % 13, n, count, dtype, std=1e-2)
