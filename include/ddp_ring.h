@@ -259,9 +259,13 @@ int ring_reduce_scatter_fused(const void* const* bufs, void* const* shards, int3
  * ddp_sync: one DDP gradient synchronisation. For every bucket b in plan
  * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_FUSED,
  * _STEPS or _PERSISTENT) on bucket b's N buffers, bucket_unpack_scale with
- * `scale` (pass 1/N for DDP's mean); or, for DDP_VARIANT_VIEW,
- * bucket_allreduce_view on the gradients themselves. Bucket i+1 is never
- * started before bucket i ([R] section 03).
+ * `scale` (pass 1/N for DDP's mean). Bucket i+1 is never started before
+ * bucket i ([R] section 03). For DDP_VARIANT_VIEW the gradients themselves
+ * are reduced in place, all buckets in one launch over the arenas (every
+ * bucket is ready when ddp_sync is called): each element is summed in its
+ * own bucket's chunk order, so the result is bit for bit that of
+ * bucket_allreduce_view on every bucket. To sync buckets as they become
+ * ready, use the reducer below.
  *   grad_arenas[N]: as for bucket_pack.
  *   bucket_bufs[B*N]: bucket b of rank r at index b*N + r (host array); may
  *       be NULL for DDP_VARIANT_VIEW.

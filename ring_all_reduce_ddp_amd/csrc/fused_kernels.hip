@@ -94,9 +94,7 @@ __global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_staged
   const uint32_t* words = reinterpret_cast<const uint32_t*>(stage);
   uint32_t* result = reinterpret_cast<uint32_t*>(stage);
   for (int d = threadIdx.x; d < kWords; d += W * kFusedThreads) {
-    typename Wd::Acc a = Wd::from(words[first * kWords + d]);
-    for (int k = 1; k < n; ++k) Wd::add(a, words[wrap(first + k, n) * kWords + d]);
-    result[d] = Wd::out(a);
+    result[d] = Wd::out(ring_sum_rows<DT, NR>(words, kWords, first, n, d));
   }
   __syncthreads();
   if (!mine) return;

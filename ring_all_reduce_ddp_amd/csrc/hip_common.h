@@ -55,6 +55,8 @@ int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status)
 int launch_view_bucket(const ddp_plan* plan, int32_t b, const RankPtrs& P, int32_t N, float scale,
                        int64_t max_blocks, hipStream_t s);
 int check_view_arenas(const ddp_plan* plan, void* const* grad_arenas, int32_t N, const char* fn);
+// The in-place sync of every bucket at once: one launch over the whole arena.
+int launch_view_arena(const ddp_plan* plan, const RankPtrs& P, int32_t N, float scale, hipStream_t s);
 
 // The synthetic backward kernel on already-checked buffers (runtime.hip).
 int launch_synthetic_backward(const RankPtrs& S, const RankPtrs& D, int32_t N, int64_t numel, int32_t dtype,

@@ -303,13 +303,14 @@ extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* co
     return fail(DDP_EINVAL, std::string(fn) + ": pointer array is NULL");
   if (N != plan->world_size) return fail(DDP_EINVAL, std::string(fn) + ": N differs from the plan's world size");
   if (variant == DDP_VARIANT_VIEW) {
-    if (plan->comm_dtype != plan->dtype)
-      return fail(DDP_EINVAL, std::string(fn) + ": the in-place sync needs buckets of the gradients' dtype");
-    for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
-      int st = bucket_allreduce_view(plan, b, grad_arenas, N, scale, stream);
-      if (st != DDP_OK) return st;
-    }
-    return DDP_OK;
+    // Every bucket is ready, so one launch covers the whole arena: each
+    // element still takes its own bucket's chunk and ring order (the arena
+    // map), so the result is that of the bucket-by-bucket sync.
+    int st = check_view_arenas(plan, grad_arenas, N, fn);
+    if (st != DDP_OK) return st;
+    RankPtrs P{};
+    for (int r = 0; r < N; ++r) P.p[r] = grad_arenas[r];
+    return launch_view_arena(plan, P, N, scale, as_stream(stream));
   }
   for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
     void* const* bufs = bucket_bufs + size_t(b) * N;

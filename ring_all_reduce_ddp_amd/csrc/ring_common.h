@@ -51,6 +51,33 @@ __device__ __forceinline__ int64_t tile_vector(int64_t lo, int64_t t, int thread
   return (lo / tile + t) * threads + threadIdx.x;
 }
 
+// Word d of a staged tile summed down the LDS rows (one row of `row_words`
+// words per rank) in ring order: row `first`, then first+1, ..., first+n-1
+// (mod n), one rounding per add. With a compile-time rank count the loop
+// unrolls; otherwise rows are read eight at a time, so their LDS reads are in
+// flight together instead of one round trip per rank.
+template <int DT, int NR>
+__device__ __forceinline__ typename Word<DT>::Acc ring_sum_rows(const uint32_t* words, int row_words, int first,
+                                                               int n, int d) {
+  using Wd = Word<DT>;
+  typename Wd::Acc a = Wd::from(words[first * row_words + d]);
+  if constexpr (NR > 0) {
+#pragma unroll
+    for (int k = 1; k < NR; ++k) Wd::add(a, words[wrap(first + k, NR) * row_words + d]);
+  } else {
+    int k = 1;
+    for (; k + 8 <= n; k += 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = words[wrap(first + k + j, n) * row_words + d];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Wd::add(a, x[j]);
+    }
+    for (; k < n; ++k) Wd::add(a, words[wrap(first + k, n) * row_words + d]);
+  }
+  return a;
+}
+
 inline unsigned grid_for(int64_t total_tiles) {
   return unsigned(std::max<int64_t>(1, std::min(total_tiles, kMaxGrid)));
 }

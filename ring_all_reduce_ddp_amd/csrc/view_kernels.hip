@@ -87,9 +87,7 @@ __device__ __forceinline__ void view_tile(int64_t tile, const uint16_t* info, in
     const int c = info_of[d >> 2] & 0xff;
     if (c == 0xff) continue;  // padding between members
     const int first = wrap(c + 1, n);
-    typename Wd::Acc a = Wd::from(words[first * kWords + d]);
-    for (int k = 1; k < n; ++k) Wd::add(a, words[wrap(first + k, n) * kWords + d]);
-    result[d] = Wd::out(a, scale);
+    result[d] = Wd::out(ring_sum_rows<DT, NR>(words, kWords, first, n, d), scale);
   }
   __syncthreads();
   const uint16_t g = info_of[lane];
@@ -202,6 +200,26 @@ int launch_view_bucket(const ddp_plan* plan, int32_t b, const RankPtrs& P, int32
     else launch_view<DDP_BF16, false>(sp, P, N, scale, max_blocks, s);
   }
   DDP_HIP_TRY(hipGetLastError(), "bucket_allreduce_view: launch");
+  return DDP_OK;
+}
+
+int launch_view_arena(const ddp_plan* plan, const RankPtrs& P, int32_t N, float scale, hipStream_t s) {
+  const int64_t vecs = int64_t(plan->vec_info.size());
+  if (vecs == 0) return DDP_OK;
+  const uint16_t* info = nullptr;
+  int st = device_tables(const_cast<ddp_plan*>(plan), nullptr, &info);
+  if (st != DDP_OK) return st;
+  const int eb = elem_bytes(plan->dtype);
+  const bool ntl = int64_t(N) * plan->arena_numel * eb > kViewCacheResidentBytes;
+  const ViewSpan sp{info, 0, (vecs + kViewThreads - 1) / kViewThreads, 0, vecs};
+  if (plan->dtype == DDP_FP32) {
+    if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, 0, s);
+    else launch_view<DDP_FP32, false>(sp, P, N, scale, 0, s);
+  } else {
+    if (ntl) launch_view<DDP_BF16, true>(sp, P, N, scale, 0, s);
+    else launch_view<DDP_BF16, false>(sp, P, N, scale, 0, s);
+  }
+  DDP_HIP_TRY(hipGetLastError(), "ddp_sync: launch");
   return DDP_OK;
 }
 
