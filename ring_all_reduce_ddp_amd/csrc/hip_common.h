@@ -64,13 +64,18 @@ int launch_synthetic_backward(const RankPtrs& S, const RankPtrs& D, int32_t N, i
 
 // ---------------------------------------------------------------- device helpers
 
-// Round an fp32 value to the nearest bf16 (ties to even) and return the bf16
-// as an fp32 value with its low 16 bits clear. NaN stays a quiet NaN.
-__device__ __forceinline__ float round_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return __uint_as_float((u | 0x00400000u) & 0xffff0000u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
+// fp32 to bf16, round to nearest with ties to even, by gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32, two values at once). Subnormals are kept,
+// infinities and overflow give infinity, and a NaN stays a NaN with its quiet
+// bit set and its upper payload bits kept. On MI355X it gave the same bits
+// as the bit-level definition (add 0x7fff plus the lowest kept bit, then
+// truncate; NaN: set the quiet bit, truncate) for all 2^32 fp32 inputs.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 and packed: `lo` in bits 0-15, `hi` in 16-31.
+__device__ __forceinline__ uint32_t round_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -78,6 +83,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
+
+// One fp32 value rounded to bf16, returned as an fp32 value with its low 16
+// bits clear.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_lo(round_bf16x2(f, 0.0f)); }
 
 // Per-dtype arithmetic on 16-byte vectors and on single elements. An
 // accumulator holds values of the buffer dtype (bf16 values are kept as fp32
@@ -132,22 +141,23 @@ struct Ops<DDP_BF16> {
     return Acc{{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), bf16_lo(w.z),
                 bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)}};
   }
+  static __device__ __forceinline__ void add2(float& lo, float& hi, uint32_t w) {
+    const uint32_t r = round_bf16x2(lo + bf16_lo(w), hi + bf16_hi(w));
+    lo = bf16_lo(r);
+    hi = bf16_hi(r);
+  }
   static __device__ __forceinline__ void add(Acc& a, u32x4 w) {
-    a.v[0] = round_bf16(a.v[0] + bf16_lo(w.x));
-    a.v[1] = round_bf16(a.v[1] + bf16_hi(w.x));
-    a.v[2] = round_bf16(a.v[2] + bf16_lo(w.y));
-    a.v[3] = round_bf16(a.v[3] + bf16_hi(w.y));
-    a.v[4] = round_bf16(a.v[4] + bf16_lo(w.z));
-    a.v[5] = round_bf16(a.v[5] + bf16_hi(w.z));
-    a.v[6] = round_bf16(a.v[6] + bf16_lo(w.w));
-    a.v[7] = round_bf16(a.v[7] + bf16_hi(w.w));
+    add2(a.v[0], a.v[1], w.x);
+    add2(a.v[2], a.v[3], w.y);
+    add2(a.v[4], a.v[5], w.z);
+    add2(a.v[6], a.v[7], w.w);
   }
   static __device__ __forceinline__ u32x4 to(const Acc& a) {
     return u32x4{bf16_pack(a.v[0], a.v[1]), bf16_pack(a.v[2], a.v[3]), bf16_pack(a.v[4], a.v[5]),
                  bf16_pack(a.v[6], a.v[7])};
   }
   static __device__ __forceinline__ uint32_t scale2(uint32_t w, float s) {
-    return bf16_pack(round_bf16(bf16_lo(w) * s), round_bf16(bf16_hi(w) * s));
+    return round_bf16x2(bf16_lo(w) * s, bf16_hi(w) * s);
   }
   static __device__ __forceinline__ u32x4 scale(u32x4 w, float s) {
     return u32x4{scale2(w.x, s), scale2(w.y, s), scale2(w.z, s), scale2(w.w, s)};
@@ -194,12 +204,13 @@ struct Word<DDP_BF16> {
   };
   static __device__ __forceinline__ Acc from(uint32_t w) { return Acc{bf16_lo(w), bf16_hi(w)}; }
   static __device__ __forceinline__ void add(Acc& a, uint32_t w) {
-    a.lo = round_bf16(a.lo + bf16_lo(w));
-    a.hi = round_bf16(a.hi + bf16_hi(w));
+    const uint32_t r = round_bf16x2(a.lo + bf16_lo(w), a.hi + bf16_hi(w));
+    a.lo = bf16_lo(r);
+    a.hi = bf16_hi(r);
   }
   static __device__ __forceinline__ uint32_t out(const Acc& a) { return bf16_pack(a.lo, a.hi); }
   static __device__ __forceinline__ uint32_t out(const Acc& a, float s) {
-    return bf16_pack(round_bf16(a.lo * s), round_bf16(a.hi * s));
+    return round_bf16x2(a.lo * s, a.hi * s);
   }
   static __device__ __forceinline__ float elem(u32x4 y, int j) {
     return (j & 1) ? bf16_hi(y[j >> 1]) : bf16_lo(y[j >> 1]);

@@ -113,10 +113,10 @@ __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* se
       if (e + V <= sg.numel) {
         const u32x4* src = reinterpret_cast<const u32x4*>(arena + sg.src_off + e);
         const u32x4 a = src[0], b = src[1];
-        *d = u32x4{bf16_pack(round_bf16(__uint_as_float(a.x)), round_bf16(__uint_as_float(a.y))),
-                   bf16_pack(round_bf16(__uint_as_float(a.z)), round_bf16(__uint_as_float(a.w))),
-                   bf16_pack(round_bf16(__uint_as_float(b.x)), round_bf16(__uint_as_float(b.y))),
-                   bf16_pack(round_bf16(__uint_as_float(b.z)), round_bf16(__uint_as_float(b.w)))};
+        *d = u32x4{round_bf16x2(__uint_as_float(a.x), __uint_as_float(a.y)),
+                   round_bf16x2(__uint_as_float(a.z), __uint_as_float(a.w)),
+                   round_bf16x2(__uint_as_float(b.x), __uint_as_float(b.y)),
+                   round_bf16x2(__uint_as_float(b.z), __uint_as_float(b.w))};
       } else if (e >= sg.numel) {
         *d = u32x4{0u, 0u, 0u, 0u};
       } else {

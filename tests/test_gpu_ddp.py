@@ -247,3 +247,34 @@ def test_view_sync_leaves_slack_alone(dtype):
     torch.cuda.synchronize()
     for r, a in enumerate(arenas):
         assert_bit_equal(to_host(a, dtype)[slack], before[r], f"slack of rank {r}")
+
+
+def test_bf16_compression_rounding_on_bit_patterns():
+    """Packing fp32 gradients into bf16 buckets rounds exactly as the oracle
+    does, on 2^22 random fp32 bit patterns (every exponent, subnormals, NaNs,
+    infinities) plus hand-picked halfway, overflow and subnormal cases. NaNs
+    are compared by position only: the oracle's NaN is canonical, the
+    kernel keeps the payload's upper bits (reading 4 of the design notes)."""
+    edge = np.array([0x00000000, 0x80000000, 0x00000001, 0x00008000, 0x00018000, 0x007fffff,
+                     0x00807fff, 0x00808000, 0x00818000, 0x3f808000, 0x3f818000, 0x3f807fff,
+                     0x7f7f7fff, 0x7f7f8000, 0x7f7fffff, 0xff7fffff, 0x7f800000, 0xff800000,
+                     0x7fc00000, 0x7f800001, 0xffc12345, 0x7fffffff], dtype=np.uint32)
+    rng = np.random.default_rng(2024)
+    pats = np.concatenate([edge, rng.integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)])
+    g = pats.view(np.float32)
+    numels = [len(g)]
+    plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=1)
+    arenas, offs = make_arenas(plan, [[g]], "fp32")
+    padded, _ = plan.bucket(0)
+    bucket = [torch.empty(padded, dtype=torch.bfloat16, device="cuda")]
+    rar.bucket_pack(plan, 0, arenas, bucket)
+    torch.cuda.synchronize()
+    got = to_host(bucket[0], "bf16")[:len(g)]
+    oplan = planner.plan(numels, 4, world_size=1, vector_elems=8)
+    with np.errstate(invalid="ignore", over="ignore"):
+        want = ddp.pack([g], oplan[0], "bf16", "fp32")[:len(g)]
+    got_nan = (got & 0x7fff) > 0x7f80
+    want_nan = (want & 0x7fff) > 0x7f80
+    assert np.array_equal(got_nan, want_nan)
+    assert np.array_equal(got[~got_nan], want[~want_nan])
+    assert got_nan.sum() > 1000   # the sample does hold NaNs
