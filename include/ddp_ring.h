@@ -288,8 +288,9 @@ int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket
  *   the reducer. For DDP_VARIANT_VIEW the arenas are checked here, once, and
  *   must stay allocated while the reducer exists.
  *   comm_max_blocks (DDP_VARIANT_VIEW only; 0 for no limit): the syncs of all
- *   buckets but the last run on at most this many one-wave blocks, so they
- *   take few of the compute units that backward is still using (the way a
+ *   buckets but the last run on at most this many blocks (of min(N, 8)
+ *   waves each), so they take few of the compute units that backward is
+ *   still using (the way a
  *   collective library limits the channels a collective occupies); the last
  *   bucket, ready only once backward is over, runs full width. Results do not
  *   depend on it.

@@ -22,10 +22,10 @@ namespace {
 // every eighth rank). Wave w loads rank w's tile into LDS row w, the block
 // sums each 32-bit word down the rows in ring order, and wave w stores the
 // result to rank w: every wave streams one rank's buffer, one load and one
-// store per lane. That ran at 6.1-6.2 TB/s, where one-wave blocks that each
-// read all N ranks and write all N ranks reached 5.7-5.8 TB/s on the same
-// parts; the staged form also leaves far more room to a compute kernel
-// running beside it on another stream. Tiles go chunk by chunk (chunk-major
+// store per lane. That ran at 6.3-6.4 TB/s, where one-wave blocks that each
+// read all N ranks and write all N ranks reached 5.7-5.9 TB/s on the same
+// parts (the best copy kernel: 6.7 TB/s); the staged form also leaves far
+// more room to a compute kernel running beside it on another stream. Tiles go chunk by chunk (chunk-major
 // and chunk-interleaved orders ran alike at 1 GiB, chunk-major faster at
 // 24 MiB per rank). Stores are non-temporal (the result is not read again
 // here); loads are too when the N buffers together exceed the 256 MB
