@@ -1,0 +1,68 @@
+"""GPU parity where one chunk (fused all-reduce) or one arena (in-place sync)
+has more tiles than one launch's grid holds (2^22 tiles), so the launcher
+splits the work over several launches. Two ranks, fp32, 8.6 GB and 4.3 GB
+per rank; sampled positions, including both sides of every split, against
+the oracle. Memory: ~17 GB of HBM for the first test, ~9 GB for the second."""
+
+import numpy as np
+import pytest
+import torch
+
+import ring_all_reduce_ddp_amd as rar
+from oracle import ring, rounding
+from ddp_workloads import device_ring_inputs
+
+from gpu_util import assert_bit_equal, sample_positions, gather
+
+pytestmark = pytest.mark.gpu
+
+MAX_GRID_TILES = 1 << 22   # tiles per launch, at most
+TILE_FP32 = 256            # fp32 elements per rank in one tile (64 lanes x 16 bytes)
+
+
+def with_edges(pos, count, splits):
+    extra = np.array([s + d for s in splits for d in (-2, -1, 0, 1)], dtype=np.int64)
+    pos = np.concatenate([pos, extra])
+    return np.unique(pos[(pos >= 0) & (pos < count)])
+
+
+def test_fused_all_reduce_split_over_launches():
+    n = 2
+    L = MAX_GRID_TILES * TILE_FP32 + 4096   # one chunk needs two launches
+    count = n * L
+    bufs = device_ring_inputs(31, n, count, "fp32", std=1e-3)
+    pos = with_edges(sample_positions(count, n, 20000, seed=31), count,
+                     [c * L + MAX_GRID_TILES * TILE_FP32 for c in range(n)])
+    pos_dev = torch.from_numpy(pos).cuda()
+    before = [gather(t, pos_dev, "fp32") for t in bufs]
+    print(f"[fused split] N={n} count={count} samples={len(pos)}", flush=True)
+    rar.ring_allreduce_fused(bufs)
+    torch.cuda.synchronize()
+    after = [gather(t, pos_dev, "fp32") for t in bufs]
+    want = ring.ring_simulate(before, "fp32", chunk_of=pos // L)["bufs"]
+    for r in range(n):
+        assert_bit_equal(after[r], want[r], f"rank {r}")
+
+
+def test_in_place_sync_split_over_launches():
+    n = 2
+    numel = MAX_GRID_TILES * TILE_FP32 + 1001   # arena tiles beyond one launch; a ragged last vector
+    plan = rar.ddp_bucket_plan([numel], "fp32", cap_bytes=1 << 40, first_bucket_bytes=1 << 40, world_size=n)
+    arena_numel, offs = plan.grad_arena()
+    assert offs[0] == 0 and arena_numel >= numel
+    arenas = device_ring_inputs(32, n, arena_numel, "fp32", std=1e-3)
+    padded, _ = plan.bucket(0)
+    L = padded // n
+    pos = with_edges(sample_positions(numel, n, 20000, seed=32), numel, [MAX_GRID_TILES * TILE_FP32, L])
+    pos_dev = torch.from_numpy(pos).cuda()
+    before = [gather(t, pos_dev, "fp32") for t in arenas]
+    tail = [t[numel:].clone() for t in arenas]   # alignment padding after the member
+    print(f"[in-place split] N={n} numel={numel} samples={len(pos)}", flush=True)
+    rar.ddp_sync(plan, arenas, None, variant="view", scale=0.5)
+    torch.cuda.synchronize()
+    after = [gather(t, pos_dev, "fp32") for t in arenas]
+    summed = ring.ring_simulate(before, "fp32", chunk_of=pos // L)["bufs"]
+    want = rounding.round_to_fp32(rounding.to_f64(summed[0], "fp32") * 0.5)
+    for r in range(n):
+        assert_bit_equal(after[r], want, f"rank {r}")
+        assert torch.equal(arenas[r][numel:], tail[r]), "padding after the member was written"
