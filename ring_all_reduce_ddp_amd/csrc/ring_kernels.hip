@@ -32,7 +32,14 @@ namespace {
 
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
 constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
-constexpr int kPersistentBlocksPerCU = 2;  // default persistent grid: 512 blocks on 256 CUs
+// Persistent grid, measured on MI355X at 8 x 1 GiB fp32 (14 steps): 1024-thread
+// blocks, three for every four compute units (192 blocks): 6.52 ms. With
+// 1024-thread blocks, 160 to 256 blocks took 6.65, 6.54, 6.52, 6.77, 6.96,
+// 7.08 and 7.23 ms; 256 blocks of 512 threads 6.65 ms; 512 blocks of 256
+// threads 6.96 ms. More blocks add barrier arrivals and polling; fewer leave
+// bandwidth unused.
+constexpr int kPersistentThreads = 1024;   // threads per persistent block
+constexpr int kPersistentBlocksPer4CUs = 3;
 
 // ---------------------------------------------------------------- one step
 
@@ -161,7 +168,7 @@ __device__ bool grid_barrier(unsigned int* counter, unsigned int target, unsigne
 // added to every barrier's expected arrival count; it is non-zero only when
 // a test forces the time-out path.
 template <int DT, bool VEC, bool NT>
-__global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int64_t count, int64_t L,
+__global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, int n, int64_t count, int64_t L,
                                                          int64_t tiles_per_chunk, int n_steps,
                                                          unsigned int* counter, unsigned int* status,
                                                          unsigned long long deadline, unsigned int extra) {
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int6
     const int phase = i < n - 1 ? DDP_RS : DDP_AG;
     const int s = i < n - 1 ? i : i - (n - 1);
     for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
-      step_tile<DT, VEC, kThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
+      step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
     if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
       return;
   }
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_persistent(RankPtrs P, int n, int6
 // Tiles per chunk of the persistent kernel (256 threads x kStepUnroll vectors).
 template <int DT>
 int64_t step_tiles_per_chunk(const RingArgs& a) {
-  const int64_t tile = a.vec ? int64_t(kThreads) * kStepUnroll * Ops<DT>::V : kThreads;
+  const int64_t tile = a.vec ? int64_t(kPersistentThreads) * kStepUnroll * Ops<DT>::V : kPersistentThreads;
   return aligned_tiles_per_chunk(a.L, tile);
 }
 
@@ -208,18 +215,20 @@ int launch_step(const RingArgs& a, int step, int phase, hipStream_t s) {
 }
 
 struct PersistentOpts {
-  int32_t max_blocks = 0;       // 0: kPersistentBlocksPerCU blocks per compute unit
+  int32_t max_blocks = 0;       // 0: the default grid (see persistent_grid)
   int64_t timeout_us = kDefaultTimeoutUs;
   uint32_t extra_arrivals = 0;  // test hook: forces the time-out path
 };
 
-// Grid of the persistent kernel: kPersistentBlocksPerCU blocks per compute
-// unit (or max_blocks if > 0), never more than one block per tile of a step,
+// Grid of the persistent kernel: kPersistentBlocksPer4CUs blocks per four
+// compute units (or max_blocks if > 0), never more than one block per tile of a step,
 // and never more than (occupancy - 1) blocks per compute unit. The headroom
-// is measured, not cosmetic: on MI355X the occupancy query reports 8 blocks
-// of this kernel per CU, yet a 2048-block cooperative grid had only 1792
-// blocks (7 per CU) running at the first barrier; the other 256 could not
-// start until those left, so the barrier could never complete.
+// is measured, not cosmetic: on MI355X the occupancy query reported 8 blocks
+// per CU for this kernel with 256-thread blocks, yet a 2048-block cooperative
+// grid had only 1792 blocks (7 per CU) running at the first barrier; the
+// other 256 could not start until those left, so the barrier could never
+// complete. (With 1024-thread blocks the query reports 1 per CU, its
+// register limit, and the clamp is then one block per CU.)
 template <int DT, bool VEC, bool NT>
 int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* cus) {
   const int64_t total = step_tiles_per_chunk<DT>(a) * a.n;
@@ -228,12 +237,13 @@ int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* 
   DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent: hipGetDevice");
   DDP_HIP_TRY(hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev),
               "ring_allreduce_persistent: multiprocessor count");
-  DDP_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0),
+  DDP_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kPersistentThreads, 0),
               "ring_allreduce_persistent: occupancy");
   if (per_cu < 1 || *cus < 1)
     return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: no block can be resident");
   const int64_t safe = int64_t(per_cu > 1 ? per_cu - 1 : 1) * (*cus);
-  const int64_t want = max_blocks > 0 ? int64_t(max_blocks) : int64_t(kPersistentBlocksPerCU) * (*cus);
+  const int64_t want =
+      max_blocks > 0 ? int64_t(max_blocks) : std::max<int64_t>(1, int64_t(kPersistentBlocksPer4CUs) * (*cus) / 4);
   *grid = unsigned(std::max<int64_t>(1, std::min({total, want, safe})));
   return DDP_OK;
 }
@@ -261,7 +271,7 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
       (unsigned long long)(std::max<int64_t>(clock_khz, 1)) * (unsigned long long)(o.timeout_us) / 1000ull;
   unsigned int extra = o.extra_arrivals;
   void* args[] = {&P, &n, &count, &L, &tiles, &steps, &slot, &status, &deadline, &extra};
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kPersistentThreads), args, 0, s);
   if (e == hipErrorCooperativeLaunchTooLarge) {
     (void)hipGetLastError();
     return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: grid cannot be co-resident");
