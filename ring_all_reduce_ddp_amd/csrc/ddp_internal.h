@@ -51,6 +51,7 @@ struct Bucket {
   int64_t seg_begin = 0;   // index of its first segment in plan.segments
   int64_t n_segs = 0;
   int64_t n_tiles = 0;     // pack/unpack tiles per rank
+  int64_t tile_seg_begin = 0;  // index of its first tile in plan.tile_seg
   int64_t view_vec_begin = 0;  // the bucket's members span arena vectors
   int64_t view_vec_end = 0;    // [view_vec_begin, view_vec_end) (in-place sync)
   int64_t n_view_tiles = 0;    // view tiles covering that span
@@ -61,6 +62,7 @@ constexpr int kMaxDevices = 64;
 
 struct DeviceTable {
   Segment* segs = nullptr;       // device copy of plan.segments
+  int32_t* tile_seg = nullptr;   // device copy of plan.tile_seg (same allocation)
   uint16_t* vec_info = nullptr;  // device copy of plan.vec_info (same allocation)
 };
 
@@ -77,6 +79,7 @@ struct ddp_plan {
   int64_t arena_numel = 0;
   std::vector<ddp::Bucket> buckets;
   std::vector<ddp::Segment> segments;   // all buckets' segments, bucket-major
+  std::vector<int32_t> tile_seg;        // per pack/unpack tile: its segment, counted from the bucket's first
   std::vector<uint16_t> vec_info;       // per arena vector (in-place sync; same dtypes only)
   int64_t tile_elems = 0;               // elements per pack tile (bucket vectors)
   std::mutex mu;                        // guards `device`
@@ -94,9 +97,11 @@ inline int64_t pack_tile_elems(int32_t comm_dtype) {
 }
 // Arena vectors covered by one tile of the in-place sync (one per lane of a wave).
 constexpr int kViewThreads = 64;
-// Device copies of the plan's segment table and arena vector map on the
-// current device, made on first use (defined with the HIP code).
-int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info);
+// Device copies of the plan's segment table, tile-to-segment table and arena
+// vector map on the current device, made on first use (defined with the HIP
+// code). Any output pointer may be NULL.
+int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info,
+                  const int32_t** tile_seg = nullptr);
 // Releases the device tables of a plan (defined with the HIP code).
 void release_device_tables(ddp_plan* plan);
 }  // namespace ddp

@@ -16,8 +16,8 @@
 //
 // A bucket is a list of segments (each member's slot, then the zero padding);
 // each segment is covered by whole tiles so a block never mixes segments, and
-// a block finds its segment by a uniform binary search over the tile prefix
-// sums. Members and arena offsets start on 16-byte boundaries, so everything
+// a block finds its segment with one load from the plan's tile-to-segment
+// table. Members and arena offsets start on 16-byte boundaries, so everything
 // but the last partial vector of a member moves as 16-byte vectors.
 #include <algorithm>
 
@@ -26,18 +26,8 @@
 namespace ddp {
 namespace {
 
-__device__ __forceinline__ int find_segment(const Segment* segs, int n_segs, int64_t tile) {
-  int lo = 0, hi = n_segs - 1;  // last segment whose tile_begin <= tile
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (segs[mid].tile_begin <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, int n_segs, int64_t n_tiles,
+__global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
                                                    RankPtrs arenas, RankPtrs buckets) {
   using O = Ops<DT>;
   constexpr int V = O::V;
@@ -46,17 +36,23 @@ __global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, int n_se
   const void* arena = arenas.p[blockIdx.y];
   void* bucket = buckets.p[blockIdx.y];
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const Segment sg = segs[tile_seg[tile]];
     const int64_t first = (tile - sg.tile_begin) * kTile;
+    // All of the tile's loads are issued before its first store (the
+    // compiler cannot tell the arena from the bucket, so it would not move a
+    // load above an earlier store on its own).
+    u32x4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;  // element in the slot
+      x[u] = e + V <= sg.numel ? static_cast<const u32x4*>(arena)[(sg.src_off + e) / V] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
       if (e >= sg.slot) continue;
-      u32x4* d = static_cast<u32x4*>(bucket) + (sg.dst_off + e) / V;
-      if (e + V <= sg.numel) {
-        *d = static_cast<const u32x4*>(arena)[(sg.src_off + e) / V];
-      } else if (e >= sg.numel) {
-        *d = u32x4{0u, 0u, 0u, 0u};
+      if (e + V <= sg.numel || e >= sg.numel) {
+        static_cast<u32x4*>(bucket)[(sg.dst_off + e) / V] = x[u];  // a vector of the member, or padding zeros
       } else {
         for (int i = 0; i < V; ++i)
           O::store1(bucket, sg.dst_off + e + i, e + i < sg.numel ? O::load1(arena, sg.src_off + e + i) : 0.0f);
@@ -66,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, int n_se
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, int n_segs, int64_t n_tiles,
+__global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
                                                            RankPtrs buckets, RankPtrs arenas, float scale) {
   using O = Ops<DT>;
   constexpr int V = O::V;
@@ -75,15 +71,20 @@ __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, 
   const void* bucket = buckets.p[blockIdx.y];
   void* arena = arenas.p[blockIdx.y];
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const Segment sg = segs[tile_seg[tile]];
     const int64_t first = (tile - sg.tile_begin) * kTile;
+    u32x4 x[U];  // every load before the first store, as in k_pack
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e + V <= sg.numel) x[u] = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
       if (e >= sg.numel) continue;  // padding and slack stay in the bucket
       if (e + V <= sg.numel) {
-        const u32x4 x = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
-        static_cast<u32x4*>(arena)[(sg.src_off + e) / V] = O::scale(x, scale);
+        static_cast<u32x4*>(arena)[(sg.src_off + e) / V] = O::scale(x[u], scale);
       } else {
         for (int64_t i = e; i < sg.numel; ++i)
           O::store1(arena, sg.src_off + i, O::mul1(O::load1(bucket, sg.dst_off + i), scale));
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, 
 // fp32 gradients into a bf16 bucket (the bf16 compression hook): every
 // gradient is rounded to the nearest bf16, ties to even. A bucket vector is 8
 // bf16 elements; it reads two 16-byte vectors of fp32 gradients.
-__global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* segs, int n_segs, int64_t n_tiles,
+__global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
                                                                RankPtrs arenas, RankPtrs buckets) {
   constexpr int V = 8;
   constexpr int U = kPackVecsPerThread;
@@ -103,20 +104,28 @@ __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* se
   const float* arena = static_cast<const float*>(arenas.p[blockIdx.y]);
   void* bucket = buckets.p[blockIdx.y];
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const Segment sg = segs[tile_seg[tile]];
     const int64_t first = (tile - sg.tile_begin) * kTile;
+    u32x4 a[U], b[U];  // every load before the first store, as in k_pack
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e + V <= sg.numel) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(arena + sg.src_off + e);
+        a[u] = src[0];
+        b[u] = src[1];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
       if (e >= sg.slot) continue;
       u32x4* d = static_cast<u32x4*>(bucket) + (sg.dst_off + e) / V;
       if (e + V <= sg.numel) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(arena + sg.src_off + e);
-        const u32x4 a = src[0], b = src[1];
-        *d = u32x4{round_bf16x2(__uint_as_float(a.x), __uint_as_float(a.y)),
-                   round_bf16x2(__uint_as_float(a.z), __uint_as_float(a.w)),
-                   round_bf16x2(__uint_as_float(b.x), __uint_as_float(b.y)),
-                   round_bf16x2(__uint_as_float(b.z), __uint_as_float(b.w))};
+        *d = u32x4{round_bf16x2(__uint_as_float(a[u].x), __uint_as_float(a[u].y)),
+                   round_bf16x2(__uint_as_float(a[u].z), __uint_as_float(a[u].w)),
+                   round_bf16x2(__uint_as_float(b[u].x), __uint_as_float(b[u].y)),
+                   round_bf16x2(__uint_as_float(b[u].z), __uint_as_float(b[u].w))};
       } else if (e >= sg.numel) {
         *d = u32x4{0u, 0u, 0u, 0u};
       } else {
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* se
 
 // bf16 bucket back into fp32 gradients: each bf16 value (exact in fp32) is
 // multiplied by `scale` and rounded once to fp32.
-__global__ __launch_bounds__(kThreads) void k_unpack_bf16_to_f32(const Segment* segs, int n_segs, int64_t n_tiles,
+__global__ __launch_bounds__(kThreads) void k_unpack_bf16_to_f32(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
                                                                  RankPtrs buckets, RankPtrs arenas, float scale) {
   constexpr int V = 8;
   constexpr int U = kPackVecsPerThread;
@@ -138,14 +147,20 @@ __global__ __launch_bounds__(kThreads) void k_unpack_bf16_to_f32(const Segment* 
   const void* bucket = buckets.p[blockIdx.y];
   float* arena = static_cast<float*>(arenas.p[blockIdx.y]);
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const Segment sg = segs[find_segment(segs, n_segs, tile)];
+    const Segment sg = segs[tile_seg[tile]];
     const int64_t first = (tile - sg.tile_begin) * kTile;
+    u32x4 xs[U];  // every load before the first store, as in k_pack
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
+      if (e + V <= sg.numel) xs[u] = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
       if (e >= sg.numel) continue;
       if (e + V <= sg.numel) {
-        const u32x4 x = static_cast<const u32x4*>(bucket)[(sg.dst_off + e) / V];
+        const u32x4 x = xs[u];
         u32x4* dst = reinterpret_cast<u32x4*>(arena + sg.src_off + e);
         dst[0] = u32x4{__float_as_uint(bf16_lo(x.x) * scale), __float_as_uint(bf16_hi(x.x) * scale),
                        __float_as_uint(bf16_lo(x.y) * scale), __float_as_uint(bf16_hi(x.y) * scale)};
@@ -190,33 +205,40 @@ unsigned copy_grid(int64_t tiles) { return unsigned(std::max<int64_t>(1, std::mi
 
 }  // namespace
 
-int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info) {
+int device_tables(ddp_plan* plan, const Segment** segs, const uint16_t** vec_info, const int32_t** tile_seg) {
   int dev = 0;
   DDP_HIP_TRY(hipGetDevice(&dev), "plan tables: hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "plan tables: device index beyond 64");
   std::lock_guard<std::mutex> lock(plan->mu);
   DeviceTable& t = plan->device[dev];
   const size_t seg_bytes = size_t(round_up(int64_t(sizeof(Segment) * plan->segments.size()), 256));
+  const size_t ts_bytes = size_t(round_up(int64_t(sizeof(int32_t) * plan->tile_seg.size()), 256));
   const size_t map_bytes = sizeof(uint16_t) * plan->vec_info.size();
-  if (t.segs == nullptr && seg_bytes + map_bytes > 0) {
+  if (t.segs == nullptr && seg_bytes + ts_bytes + map_bytes > 0) {
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, seg_bytes + map_bytes);
+    hipError_t e = hipMalloc(&p, seg_bytes + ts_bytes + map_bytes);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return fail(DDP_ENOMEM, std::string("plan tables: hipMalloc: ") + hipGetErrorString(e));
     }
-    e = hipMemcpy(p, plan->segments.data(), sizeof(Segment) * plan->segments.size(), hipMemcpyHostToDevice);
+    char* base = static_cast<char*>(p);
+    e = hipMemcpy(base, plan->segments.data(), sizeof(Segment) * plan->segments.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !plan->tile_seg.empty())
+      e = hipMemcpy(base + seg_bytes, plan->tile_seg.data(), sizeof(int32_t) * plan->tile_seg.size(),
+                    hipMemcpyHostToDevice);
     if (e == hipSuccess && map_bytes > 0)
-      e = hipMemcpy(static_cast<char*>(p) + seg_bytes, plan->vec_info.data(), map_bytes, hipMemcpyHostToDevice);
+      e = hipMemcpy(base + seg_bytes + ts_bytes, plan->vec_info.data(), map_bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(p);
       return hip_fail(e, "plan tables: hipMemcpy");
     }
-    t.segs = static_cast<Segment*>(p);
-    t.vec_info = reinterpret_cast<uint16_t*>(static_cast<char*>(p) + seg_bytes);
+    t.segs = reinterpret_cast<Segment*>(base);
+    t.tile_seg = reinterpret_cast<int32_t*>(base + seg_bytes);
+    t.vec_info = reinterpret_cast<uint16_t*>(base + seg_bytes + ts_bytes);
   }
   if (segs) *segs = t.segs;
   if (vec_info) *vec_info = t.vec_info;
+  if (tile_seg) *tile_seg = t.tile_seg;
   return DDP_OK;
 }
 
@@ -226,6 +248,7 @@ void release_device_tables(ddp_plan* plan) {
     if (t.segs != nullptr) {
       (void)hipFree(t.segs);
       t.segs = nullptr;
+      t.tile_seg = nullptr;
       t.vec_info = nullptr;
     }
   }
@@ -243,7 +266,8 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   const Bucket& bk = plan->buckets[b];
   if (bk.n_tiles == 0) return DDP_OK;
   const Segment* segs = nullptr;
-  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr);
+  const int32_t* tile_seg = nullptr;
+  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr, &tile_seg);
   if (st != DDP_OK) return st;
   RankPtrs A{}, B{};
   for (int r = 0; r < N; ++r) {
@@ -253,11 +277,11 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
   hipStream_t s = as_stream(stream);
   if (plan->dtype != plan->comm_dtype)
-    hipLaunchKernelGGL(k_pack_f32_to_bf16, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+    hipLaunchKernelGGL(k_pack_f32_to_bf16, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin, bk.n_tiles, A, B);
   else if (plan->dtype == DDP_FP32)
-    hipLaunchKernelGGL(k_pack<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+    hipLaunchKernelGGL(k_pack<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin, bk.n_tiles, A, B);
   else
-    hipLaunchKernelGGL(k_pack<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, A, B);
+    hipLaunchKernelGGL(k_pack<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin, bk.n_tiles, A, B);
   DDP_HIP_TRY(hipGetLastError(), "bucket_pack: launch");
   return DDP_OK;
 }
@@ -270,7 +294,8 @@ extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* 
   const Bucket& bk = plan->buckets[b];
   if (bk.n_tiles == 0) return DDP_OK;
   const Segment* segs = nullptr;
-  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr);
+  const int32_t* tile_seg = nullptr;
+  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr, &tile_seg);
   if (st != DDP_OK) return st;
   RankPtrs A{}, B{};
   for (int r = 0; r < N; ++r) {
@@ -280,13 +305,13 @@ extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* 
   const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
   hipStream_t s = as_stream(stream);
   if (plan->dtype != plan->comm_dtype)
-    hipLaunchKernelGGL(k_unpack_bf16_to_f32, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs), bk.n_tiles, B,
+    hipLaunchKernelGGL(k_unpack_bf16_to_f32, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin, bk.n_tiles, B,
                        A, scale);
   else if (plan->dtype == DDP_FP32)
-    hipLaunchKernelGGL(k_unpack_scale<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs),
+    hipLaunchKernelGGL(k_unpack_scale<DDP_FP32>, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin,
                        bk.n_tiles, B, A, scale);
   else
-    hipLaunchKernelGGL(k_unpack_scale<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, int(bk.n_segs),
+    hipLaunchKernelGGL(k_unpack_scale<DDP_BF16>, g, blk, 0, s, segs + bk.seg_begin, tile_seg + bk.tile_seg_begin,
                        bk.n_tiles, B, A, scale);
   DDP_HIP_TRY(hipGetLastError(), "bucket_unpack_scale: launch");
   return DDP_OK;

@@ -140,6 +140,17 @@ extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params,
       }
       b.n_segs = int64_t(plan->segments.size()) - b.seg_begin;
       b.n_tiles = tiles;
+      // Each pack tile's segment, so a block finds it with one load.
+      b.tile_seg_begin = int64_t(plan->tile_seg.size());
+      for (int64_t i = 0; i < b.n_segs; ++i) {
+        const Segment& sg = plan->segments[size_t(b.seg_begin + i)];
+        const int64_t nt = (sg.slot + plan->tile_elems - 1) / plan->tile_elems;
+        plan->tile_seg.insert(plan->tile_seg.end(), size_t(nt), int32_t(i));
+      }
+      if (int64_t(plan->tile_seg.size()) - b.tile_seg_begin != b.n_tiles) {
+        delete plan;
+        return fail(DDP_EINVAL, "ddp_bucket_plan: internal error: tile table does not match the bucket's tiles");
+      }
 
       for (const Member& m : b.members) b.data_numel += m.numel;
       // The in-place sync (same dtypes only): the bucket's members are a run
