@@ -278,3 +278,35 @@ def test_bf16_compression_rounding_on_bit_patterns():
     assert np.array_equal(got_nan, want_nan)
     assert np.array_equal(got[~got_nan], want[~want_nan])
     assert got_nan.sum() > 1000   # the sample does hold NaNs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n", [3, 8, 13])
+@pytest.mark.parametrize("order", ["plan", "reversed"])
+def test_view_bucket_by_bucket(dtype, n, order):
+    """bucket_allreduce_view on one bucket at a time (as the reducer runs it)
+    gives the oracle's sync; buckets are disjoint, so their order does not
+    matter."""
+    numels = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5]
+    cap, first = 64 * 1024, 512
+    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+    grads = host_grads(170 + n, n, numels)
+    if dtype == "bf16":
+        from ddp_workloads.gen import to_bf16_bits
+        grads = [[to_bf16_bits(x) for x in g] for g in grads]
+        grads_f32 = [[(x.astype(np.uint32) << 16).view(np.float32) for x in g] for g in grads]
+    else:
+        grads_f32 = grads
+    arenas, offs = make_arenas(plan, grads_f32, dtype)
+    scale = float(np.float32(1) / np.float32(n))
+    buckets = list(range(plan.num_buckets))
+    if order == "reversed":
+        buckets.reverse()
+    for b in buckets:
+        rar.bucket_allreduce_view(plan, b, arenas, scale)
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, dtype)
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4 if dtype == "fp32" else 2, cap, first, n), dtype)
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"n={n} {dtype} rank {r} param {p}")
