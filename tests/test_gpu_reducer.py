@@ -137,3 +137,32 @@ def test_native_backward_pass_with_reducer(cap_mib, blocks):
     torch.cuda.synchronize()
     want = ddp.ddp_sync(grads, planner.plan(numels, 4, cap_mib << 20, 2 ** 20, n), "fp32", scale=0.125)
     check(arenas, offs, numels, want, n, f"pass with reducer, cap {cap_mib} MiB, {blocks} blocks")
+
+
+@pytest.mark.parametrize("dtype,n,blocks", [("bf16", 8, 3), ("fp32", 13, 5), ("bf16", 13, 0)])
+def test_reducer_narrow_syncs_dtypes_and_ranks(dtype, n, blocks):
+    """The reducer's in-place syncs capped to a few blocks (each block then
+    loops over tiles) for bf16 gradients and for more than eight ranks."""
+    numels = NUMELS
+    cap, first = 64 * 1024, 512
+    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+    grads = host_grads(80 + n, n, numels)
+    if dtype == "bf16":
+        from ddp_workloads.gen import to_bf16_bits
+        grads = [[to_bf16_bits(x) for x in g] for g in grads]
+        grads_f32 = [[(x.astype(np.uint32) << 16).view(np.float32) for x in g] for g in grads]
+    else:
+        grads_f32 = grads
+    arenas, offs = make_arenas(plan, grads_f32, dtype)
+    scale = float(np.float32(1) / np.float32(n))
+    red = rar.Reducer(plan, arenas, variant="view", scale=scale, comm_stream=torch.cuda.Stream(),
+                      comm_max_blocks=blocks)
+    for p in reversed(range(len(numels))):
+        red.mark_ready(p)
+    red.finalize()
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, dtype)
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4 if dtype == "fp32" else 2, cap, first, n), dtype)
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{dtype} n={n} blocks={blocks} rank {r} param {p}")
