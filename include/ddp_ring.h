@@ -23,10 +23,13 @@
  *   - Arrays of device pointers (bufs, grad_arenas, bucket_bufs) are HOST
  *     arrays; the library copies them into the kernel arguments.
  *   - All device memory belongs to the caller. The library allocates only
- *     small tables of its own: per plan, a device copy of the bucket layout
- *     (made on the first pack/unpack on a device, freed by ddp_plan_free), and
- *     per device, a few KiB of barrier and status words (kept until the process
- *     ends).
+ *     tables of its own: per plan and device, a copy of the bucket layout (a
+ *     few bytes per member and per 16 KiB of bucket) and, for plans whose
+ *     gradients and buckets share a dtype, the in-place sync's map of the
+ *     gradient arena (2 bytes per 16 bytes of one rank's arena), made on the
+ *     plan's first pack, unpack or in-place sync on that device and freed by
+ *     ddp_plan_free; and per device, a few KiB of barrier and status words
+ *     (kept until the process ends).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     and the call returns without waiting; completion follows stream order,
  *     the analogue of waiting on the collective's work handle ([D], "源码阅读路线").
@@ -190,9 +193,10 @@ int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32
                               int32_t n_steps, void* stream);
 
 /* As ring_allreduce_persistent, with the launch's knobs exposed:
- *   max_blocks: cooperative grid size (0: two blocks per compute unit, the
- *       default); it is never more than one block per tile of a step, nor
- *       more than one block per compute unit below the occupancy limit;
+ *   max_blocks: cooperative grid size (0: the default, three 1024-thread
+ *       blocks for every four compute units); it is never more than one
+ *       block per tile of a step, nor more than one block per compute unit
+ *       below the occupancy limit (at least one per compute unit);
  *   timeout_us: how long a block waits at a grid barrier before the launch
  *       gives up (ring_allreduce_persistent uses 10 s); in (0, 3600 s];
  *   extra_arrivals: added to every barrier's expected arrival count. It must
