@@ -110,8 +110,35 @@ def pin_ddp_mean():
     return True
 
 
+def pin_reduce_scatter():
+    for n, count in ((3, 6), (4, 10), (8, 64), (8, 3)):
+        bufs = [host_rank_rng(300 + n, r).integers(-1000, 1001, count).astype(np.float32) for r in range(n)]
+        total = np.sum(np.stack(bufs).astype(np.int64), axis=0)
+        for scale, div in ((1.0, 1), (0.25, 4)):
+            shards = ring.reduce_scatter(bufs, "fp32", scale)
+            for r in range(n):
+                lo, hi = ring.chunk_bounds(count, n, r)
+                if len(shards) != n or not np.array_equal(shards[r].astype(np.float64), total[lo:hi] / div):
+                    return False
+    return True
+
+
+def pin_compressed_mean():
+    n = 4
+    numels = [7, 16, 40, 300]
+    buckets = planner.plan(numels, 4, cap_bytes=512, first_bucket_bytes=64, world_size=n, vector_elems=8)
+    grads = [[host_rank_rng(17, r).integers(-8, 9, m).astype(np.float32) for m in numels] for r in range(n)]
+    out = ddp.ddp_sync(grads, buckets, "fp32", comm_dtype="bf16")
+    for p in range(len(numels)):
+        want = np.sum(np.stack([grads[r][p] for r in range(n)]).astype(np.float64), axis=0) / n
+        if any(out[r][p].dtype != np.float32 or not np.array_equal(out[r][p].astype(np.float64), want)
+               for r in range(n)):
+            return False
+    return True
+
+
 PINS = [pin_worked_example, pin_integer_sums, pin_order_fixtures, pin_traffic,
-        pin_rounding, pin_planner, pin_ddp_mean]
+        pin_rounding, pin_planner, pin_ddp_mean, pin_reduce_scatter, pin_compressed_mean]
 
 
 def test_all_pins_hold_unmutated():
@@ -132,8 +159,21 @@ def _bf16_truncate(x64):
     return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def _unpack_ignoring_scale(flat, bucket, scale, dtype):
-    return {p: np.array(flat[off:off + m]) for p, off, m in bucket["members"]}
+def _unpack_ignoring_scale(flat, bucket, scale, dtype, grad_dtype=None):
+    return {p: rounding.round_to(rounding.to_f64(flat[off:off + m], dtype), grad_dtype or dtype)
+            for p, off, m in bucket["members"]}
+
+
+_reduce_scatter = ring.reduce_scatter
+
+
+def _reduce_scatter_unscaled(bufs, dtype, scale=1.0):
+    return _reduce_scatter(bufs, dtype, 1.0)
+
+
+def _reduce_scatter_shifted(bufs, dtype, scale=1.0):
+    shards = _reduce_scatter(bufs, dtype, scale)
+    return shards[1:] + shards[:1]   # rank c receives chunk c+1
 
 
 MUTATIONS = {
@@ -148,6 +188,8 @@ MUTATIONS = {
     "buckets in forward order": (planner, "bucket_order", lambda n: range(n)),
     "first bucket uses the regular cap": (planner, "bucket_capacity", lambda i, cap, first: cap),
     "unpack ignores the scale": (ddp, "unpack_scale", _unpack_ignoring_scale),
+    "reduce-scatter ignores the scale": (ring, "reduce_scatter", _reduce_scatter_unscaled),
+    "reduce-scatter gives rank c the next chunk": (ring, "reduce_scatter", _reduce_scatter_shifted),
 }
 
 
