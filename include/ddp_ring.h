@@ -144,6 +144,16 @@ int ddp_plan_member(const ddp_plan* plan, int32_t b, int32_t i, int32_t* param_i
  * param_offsets is not NULL, n_params offsets into the host array. */
 int ddp_plan_grad_arena(const ddp_plan* plan, int64_t* arena_numel, int64_t* param_offsets);
 
+/* The in-place sync's map of the gradient arena, one entry per 16-byte
+ * vector of one rank's arena (n = arena_numel / V entries, written to the
+ * host array `out`): 0xFFFF for a vector holding no member element (the
+ * alignment padding between parameters); otherwise the ring chunk of its
+ * bucket that holds the vector (low byte) and how many of its V elements
+ * belong to the member (high byte, V except in a member's last vector). The
+ * kernels read the device copy of this map; the accessor lets the layout be
+ * checked on the host. DDP_EINVAL for plans with buckets of another dtype. */
+int ddp_plan_arena_map(const ddp_plan* plan, uint16_t* out, int64_t n);
+
 /* ---------------------------------------------------------------- pack / unpack
  * bucket_pack: copy gradients into bucket b's flat buffer on every rank
  * (the gradient-to-bucket copy of DDP's default gradient_as_bucket_view=False,

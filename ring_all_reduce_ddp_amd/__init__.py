@@ -65,6 +65,7 @@ def _load():
         "ddp_plan_member": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i64),
                                            ctypes.POINTER(i64)]),
         "ddp_plan_grad_arena": (ctypes.c_int, [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "ddp_plan_arena_map": (ctypes.c_int, [vp, vp, i64]),
         "bucket_pack": (ctypes.c_int, [vp, i32, pp, pp, i32, vp]),
         "bucket_unpack_scale": (ctypes.c_int, [vp, i32, pp, pp, i32, f32, vp]),
         "ring_allreduce_step": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, vp]),
@@ -215,6 +216,15 @@ class Plan:
         for b in range(self.num_buckets):
             padded, members = self.bucket(b)
             out.append({"members": members, "padded_numel": padded})
+        return out
+
+    def arena_map(self):
+        """The in-place sync's per-vector arena map, as a numpy uint16 array."""
+        import numpy as np
+        n, _ = self.grad_arena()
+        v = 16 // (4 if self.dtype == DDP_FP32 else 2)
+        out = np.empty(n // v, dtype=np.uint16)
+        _check(_get_lib().ddp_plan_arena_map(self._h, out.ctypes.data_as(ctypes.c_void_p), len(out)))
         return out
 
     def grad_arena(self):

@@ -11,6 +11,7 @@
 // larger than the capacity sits alone in its bucket.
 #include <algorithm>
 #include <new>
+#include <string>
 
 #include "ddp_internal.h"
 
@@ -210,6 +211,17 @@ extern "C" int ddp_plan_member(const ddp_plan* plan, int32_t b, int32_t i, int32
   if (param_idx) *param_idx = bk.members[i].param;
   if (offset) *offset = bk.members[i].offset;
   if (numel) *numel = bk.members[i].numel;
+  return DDP_OK;
+}
+
+extern "C" int ddp_plan_arena_map(const ddp_plan* plan, uint16_t* out, int64_t n) {
+  if (plan == nullptr || (out == nullptr && n > 0)) return fail(DDP_EINVAL, "ddp_plan_arena_map: NULL argument");
+  if (plan->comm_dtype != plan->dtype)
+    return fail(DDP_EINVAL, "ddp_plan_arena_map: the plan has no in-place map (buckets of another dtype)");
+  if (n != int64_t(plan->vec_info.size()))
+    return fail(DDP_EINVAL, "ddp_plan_arena_map: n must be the arena's vector count (" +
+                                std::to_string(plan->vec_info.size()) + ")");
+  std::copy(plan->vec_info.begin(), plan->vec_info.end(), out);
   return DDP_OK;
 }
 

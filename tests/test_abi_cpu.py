@@ -207,3 +207,50 @@ def test_reducer_argument_errors():
     expect_status(lib.ddp_reducer_mark_ready(None, 0, None), rar.DDP_EINVAL, "NULL")
     expect_status(lib.ddp_synthetic_backward(bufs, bufs, 2, 10, rar.DDP_FP32, -1, 0, None), rar.DDP_EINVAL, "work")
     expect_status(lib.ddp_synthetic_backward(bufs, bufs, 2, 10, rar.DDP_FP32, 1, 65, None), rar.DDP_EINVAL, "lds_kib")
+
+
+def expected_arena_map(numels, elem_bytes, cap, first, n):
+    """The in-place sync's per-vector map, derived from the oracle's plan and
+    an arena laid out in registration order on V-element boundaries."""
+    v = 16 // elem_bytes
+    offs = np.concatenate([[0], np.cumsum([-(-m // v) * v for m in numels])]).astype(np.int64)
+    out = np.full(int(offs[-1]) // v, 0xFFFF, dtype=np.uint16)
+    for b in planner.plan(numels, elem_bytes, cap, first, n):
+        L = b["padded_numel"] // n
+        for p, off, m in b["members"]:
+            for e in range(0, m, v):
+                out[(offs[p] + e) // v] = ((off + e) // L) | (min(v, m - e) << 8)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_arena_map_matches_oracle_plan(seed):
+    """The map the in-place kernels read (chunk and member elements of every
+    arena vector) follows from the oracle's bucket plan."""
+    rng = np.random.default_rng(2000 + seed)
+    numels = [int(x) for x in rng.integers(0, 3000, size=rng.integers(1, 40))]
+    dt = ["fp32", "bf16"][seed % 2]
+    eb = 4 if dt == "fp32" else 2
+    cap = int(rng.integers(64, 20000))
+    first = int(rng.integers(64, 20000))
+    n = [1, 2, 3, 8, 13, 64][seed % 6]
+    p = rar.ddp_bucket_plan(numels, dt, cap, first, n)
+    assert np.array_equal(p.arena_map(), expected_arena_map(numels, eb, cap, first, n))
+
+
+def test_arena_map_resnet50():
+    numels = resnet50_param_numels()
+    p = rar.ddp_bucket_plan(numels, "fp32", world_size=8)
+    got = p.arena_map()
+    assert np.array_equal(got, expected_arena_map(numels, 4, 25 << 20, 1 << 20, 8))
+    assert (got != 0xFFFF).sum() == sum(-(-m // 4) for m in numels)
+
+
+def test_arena_map_errors():
+    lib = rar.lib
+    p = rar.ddp_bucket_plan([4, 8], "fp32", world_size=2)
+    out = (ctypes.c_uint16 * 4)()
+    assert lib.ddp_plan_arena_map(p.handle, out, 3) == rar.DDP_OK   # 4 + 8 fp32 elements: 3 vectors
+    expect_status(lib.ddp_plan_arena_map(p.handle, out, 2), rar.DDP_EINVAL, "vector count")
+    pc = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
+    expect_status(lib.ddp_plan_arena_map(pc.handle, out, 3), rar.DDP_EINVAL, "another dtype")
