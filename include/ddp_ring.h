@@ -203,8 +203,10 @@ int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32
                               int32_t n_steps, void* stream);
 
 /* As ring_allreduce_persistent, with the launch's knobs exposed:
- *   max_blocks: cooperative grid size (0: the default, three 1024-thread
- *       blocks for every four compute units); it is never more than one
+ *   max_blocks: cooperative grid size (0: the default, 1024-thread blocks,
+ *       three for every four compute units when the N buffers exceed the
+ *       256 MB Infinity Cache, three for every eight when they fit); it is
+ *       never more than one
  *       block per tile of a step, nor more than one block per compute unit
  *       below the occupancy limit (at least one per compute unit);
  *   timeout_us: how long a block waits at a grid barrier before the launch

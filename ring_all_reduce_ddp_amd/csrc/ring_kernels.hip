@@ -32,14 +32,19 @@ namespace {
 
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
 constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
-// Persistent grid, measured on MI355X at 8 x 1 GiB fp32 (14 steps): 1024-thread
-// blocks, three for every four compute units (192 blocks): 6.52 ms. With
-// 1024-thread blocks, 160 to 256 blocks took 6.65, 6.54, 6.52, 6.77, 6.96,
-// 7.08 and 7.23 ms; 256 blocks of 512 threads 6.65 ms; 512 blocks of 256
-// threads 6.96 ms. More blocks add barrier arrivals and polling; fewer leave
-// bandwidth unused.
+// Persistent grid, measured on MI355X (14 steps, 8 ranks): 1024-thread blocks.
+// Buffers beyond the Infinity Cache (8 x 1 GiB fp32): three blocks for every
+// four compute units (192): 6.52 ms; 160 to 256 blocks took 6.65, 6.54, 6.52,
+// 6.77, 6.96, 7.08 and 7.23 ms; 256 blocks of 512 threads 6.65 ms; 512 blocks
+// of 256 threads 6.96 ms. Buffers inside it (cached accesses): three blocks
+// for every eight compute units (96): 8 x 25 MiB 0.287 ms against 0.344 ms
+// with 192 (16, 32, 64, 128 blocks: 0.756, 0.430, 0.304, 0.295 ms); 8 x 16
+// MiB 0.217 against 0.271 ms. More blocks add barrier arrivals, polling and,
+// with cached stores, write-backs of dirty cache lines at every barrier;
+// fewer leave bandwidth unused.
 constexpr int kPersistentThreads = 1024;   // threads per persistent block
-constexpr int kPersistentBlocksPer4CUs = 3;
+constexpr int kPersistentBlocksPer8CUsStreaming = 6;
+constexpr int kPersistentBlocksPer8CUsCached = 3;
 
 // ---------------------------------------------------------------- one step
 
@@ -220,8 +225,8 @@ struct PersistentOpts {
   uint32_t extra_arrivals = 0;  // test hook: forces the time-out path
 };
 
-// Grid of the persistent kernel: kPersistentBlocksPer4CUs blocks per four
-// compute units (or max_blocks if > 0), never more than one block per tile of a step,
+// Grid of the persistent kernel: the default above for the buffers' cache
+// regime (or max_blocks if > 0), never more than one block per tile of a step,
 // and never more than (occupancy - 1) blocks per compute unit. The headroom
 // is measured, not cosmetic: on MI355X the occupancy query reported 8 blocks
 // per CU for this kernel with 256-thread blocks, yet a 2048-block cooperative
@@ -242,8 +247,8 @@ int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* 
   if (per_cu < 1 || *cus < 1)
     return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: no block can be resident");
   const int64_t safe = int64_t(per_cu > 1 ? per_cu - 1 : 1) * (*cus);
-  const int64_t want =
-      max_blocks > 0 ? int64_t(max_blocks) : std::max<int64_t>(1, int64_t(kPersistentBlocksPer4CUs) * (*cus) / 4);
+  const int per8 = NT ? kPersistentBlocksPer8CUsStreaming : kPersistentBlocksPer8CUsCached;
+  const int64_t want = max_blocks > 0 ? int64_t(max_blocks) : std::max<int64_t>(1, int64_t(per8) * (*cus) / 8);
   *grid = unsigned(std::max<int64_t>(1, std::min({total, want, safe})));
   return DDP_OK;
 }
@@ -341,11 +346,17 @@ extern "C" int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int3
   a.vec = a.L % (kVectorBytes / elem_bytes(dtype)) == 0;  // assuming 16-byte aligned buffers
   unsigned g = 0;
   int cus = 0;
-  // the grid does not depend on the cache policy: both instantiations use the same resources
-  int st = dtype == DDP_FP32 ? (a.vec ? persistent_grid<DDP_FP32, true, false>(a, 0, &g, &cus)
-                                      : persistent_grid<DDP_FP32, false, false>(a, 0, &g, &cus))
-                             : (a.vec ? persistent_grid<DDP_BF16, true, false>(a, 0, &g, &cus)
-                                      : persistent_grid<DDP_BF16, false, false>(a, 0, &g, &cus));
+  // the same choice of kernel as the launch: the default grid depends on the cache regime
+  const bool nt = a.vec && int64_t(N) * count * elem_bytes(dtype) > kCacheResidentBytes;
+  int st;
+  if (dtype == DDP_FP32)
+    st = !a.vec ? persistent_grid<DDP_FP32, false, false>(a, 0, &g, &cus)
+                : nt ? persistent_grid<DDP_FP32, true, true>(a, 0, &g, &cus)
+                     : persistent_grid<DDP_FP32, true, false>(a, 0, &g, &cus);
+  else
+    st = !a.vec ? persistent_grid<DDP_BF16, false, false>(a, 0, &g, &cus)
+                : nt ? persistent_grid<DDP_BF16, true, true>(a, 0, &g, &cus)
+                     : persistent_grid<DDP_BF16, true, false>(a, 0, &g, &cus);
   if (st != DDP_OK) return st;
   *grid = int32_t(g);
   if (compute_units) *compute_units = cus;
