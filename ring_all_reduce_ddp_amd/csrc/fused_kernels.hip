@@ -112,8 +112,89 @@ __global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_staged
   }
 }
 
+// Chunk lengths that are not whole 16-byte vectors (an all-reduce of any
+// count; DDP buckets are padded and never need this): the tiles run over the
+// whole buffer from its 16-byte aligned start, so loads and stores stay
+// 16-byte vectors and staged as above, and in the sum each element takes the
+// ring order of its own chunk (a tile is never shorter than a chunk here, so
+// it crosses at most one chunk boundary). A bf16 word whose two elements lie
+// in different chunks sums each half in its own order.
+template <int DT, int NR, bool NTL>
+__global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_any(RankPtrs P, int n_rt, int64_t count,
+                                                                            int64_t L, int64_t t0) {
+  using O = Ops<DT>;
+  using Wd = Word<DT>;
+  constexpr int V = O::V;
+  constexpr int W = NR > 0 ? NR : kFusedMaxWaves;
+  constexpr int kSlots = NR > 0 ? 1 : DDP_MAX_RANKS / kFusedMaxWaves;
+  constexpr int kWords = kFusedThreads * 4;
+  constexpr int EPW = V / 4;  // elements per 32-bit word: 1 for fp32, 2 for bf16
+  u32x4* stage = staged_tile<NR>();
+  const int n = NR > 0 ? NR : n_rt;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kFusedThreads);
+  const int lane = int(threadIdx.x) % kFusedThreads;
+  const int64_t tile = t0 + blockIdx.x;
+  const int64_t tile_e = tile * kFusedThreads * V;  // the tile's first element
+  const int64_t vi = tile * kFusedThreads + lane;
+  const int64_t e0 = vi * V;
+  const bool mine = e0 < count;
+  const bool full = e0 + V <= count;
+  if (mine) {
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int r = wave + j * W;
+      if (r < n) {
+        const u32x4* src = static_cast<const u32x4*>(P.p[r]);
+        stage[r * kFusedThreads + lane] = full ? ld16<NTL>(src + vi) : Wd::load_partial(src, e0, int(count - e0));
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t c0 = tile_e / L;  // chunk of the tile's first element
+  const int64_t next = (c0 + 1) * L;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(stage);
+  uint32_t* result = reinterpret_cast<uint32_t*>(stage);
+  for (int d = threadIdx.x; d < kWords; d += W * kFusedThreads) {
+    const int64_t e = tile_e + int64_t(d) * EPW;  // first element of word d
+    if (e >= count) continue;
+    const int c = int(c0) + (e >= next ? 1 : 0);
+    if constexpr (EPW == 1) {
+      result[d] = Wd::out(ring_sum_rows<DT, NR>(words, kWords, wrap(c + 1, n), n, d));
+    } else {
+      const int c_hi = int(c0) + (e + 1 >= next ? 1 : 0);
+      if (c_hi == c || e + 1 >= count) {
+        result[d] = Wd::out(ring_sum_rows<DT, NR>(words, kWords, wrap(c + 1, n), n, d));
+      } else {
+        // Each half in its own chunk's order, one rounding per add.
+        const int f_lo = wrap(c + 1, n), f_hi = wrap(c_hi + 1, n);
+        float lo = bf16_lo(words[f_lo * kWords + d]);
+        float hi = bf16_hi(words[f_hi * kWords + d]);
+        for (int k = 1; k < n; ++k) {
+          lo = round_bf16(lo + bf16_lo(words[wrap(f_lo + k, n) * kWords + d]));
+          hi = round_bf16(hi + bf16_hi(words[wrap(f_hi + k, n) * kWords + d]));
+        }
+        result[d] = bf16_pack(lo, hi);
+      }
+    }
+  }
+  __syncthreads();
+  if (!mine) return;
+  const u32x4 y = stage[lane];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int r = wave + j * W;
+    if (r >= n) continue;
+    if (full) {
+      st16<true>(static_cast<u32x4*>(P.p[r]) + vi, y);
+    } else {
+      for (int i = 0; i < int(count - e0); ++i) O::store1(P.p[r], e0 + i, Wd::elem(y, i));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- one element per thread
-// Fallback for chunks that do not start on 16-byte boundaries.
+// Fallback for buffers that do not start on 16-byte boundaries, and for
+// chunks shorter than a tile whose length is not a whole number of vectors.
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_fused_scalar(RankPtrs P, int n, int64_t count, int64_t L,
@@ -160,13 +241,47 @@ void launch_fused_vec(const RingArgs& a, hipStream_t s) {
   }
 }
 
+template <int DT, bool NTL>
+void launch_fused_any(const RingArgs& a, hipStream_t s) {
+  constexpr int V = Ops<DT>::V;
+  const int64_t tiles = (a.count + int64_t(kFusedThreads) * V - 1) / (int64_t(kFusedThreads) * V);
+  for (int64_t t0 = 0; t0 < tiles; t0 += kMaxGrid) {
+    const dim3 g(unsigned(std::min(tiles - t0, kMaxGrid)));
+    switch (a.n) {
+#define DDP_FUSED_ANY_CASE(NR)                                                                            \
+  case NR:                                                                                                \
+    hipLaunchKernelGGL((k_fused_any<DT, NR, NTL>), g, dim3(kFusedThreads * NR), 0, s, a.P, a.n, a.count,  \
+                       a.L, t0);                                                                           \
+    break;
+      DDP_FUSED_ANY_CASE(2)
+      DDP_FUSED_ANY_CASE(3)
+      DDP_FUSED_ANY_CASE(4)
+      DDP_FUSED_ANY_CASE(5)
+      DDP_FUSED_ANY_CASE(6)
+      DDP_FUSED_ANY_CASE(7)
+      DDP_FUSED_ANY_CASE(8)
+#undef DDP_FUSED_ANY_CASE
+      default:
+        hipLaunchKernelGGL((k_fused_any<DT, 0, NTL>), g, dim3(kFusedThreads * kFusedMaxWaves),
+                           size_t(a.n) * kFusedThreads * sizeof(u32x4), s, a.P, a.n, a.count, a.L, t0);
+    }
+  }
+}
+
 template <int DT>
 int launch_fused(const RingArgs& a, hipStream_t s) {
+  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kFusedCacheResidentBytes;
   if (a.vec) {
-    if (int64_t(a.n) * a.count * elem_bytes(DT) > kFusedCacheResidentBytes)
+    if (ntl)
       launch_fused_vec<DT, true>(a, s);
     else
       launch_fused_vec<DT, false>(a, s);
+  } else if (all_aligned16(const_cast<void* const*>(a.P.p), a.n) &&
+             a.L >= int64_t(kFusedThreads) * Ops<DT>::V) {
+    if (ntl)
+      launch_fused_any<DT, true>(a, s);
+    else
+      launch_fused_any<DT, false>(a, s);
   } else {
     const int64_t tpc = (a.L + kThreads - 1) / kThreads;
     const int64_t total = tpc * a.n;

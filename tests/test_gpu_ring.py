@@ -74,12 +74,16 @@ def test_c1_fused_and_exact_sum():
 
 # ---------------------------------------------------------------- small and ragged
 
-# Chunk lengths that are whole vectors take the vector kernels, the others the
-# element-wise ones; (8, 25), (6, 6141), (8, 7 * 4096 + 4093) and (9, 100_003)
-# end in a partial vector (and (8, 25) in an empty chunk) on the vector path.
+# Chunk lengths that are whole vectors take the chunk-tiled vector kernels.
+# Other lengths of at least one tile take the buffer-tiled fused kernel, in
+# which a tile may cross a chunk boundary (and, in bf16 with an odd length,
+# split a word between two chunks): (5, 12345), (7, 43019), (8, 65541),
+# (12, 36017), (33, 8482). Shorter ones take the element-wise kernels.
+# (8, 25), (6, 6141), (8, 7 * 4096 + 4093) and (9, 100_003) end in a partial
+# vector (and (8, 25) in an empty chunk) on the vector path.
 SHAPES = [(2, 4096), (3, 6), (3, 7), (4, 3), (5, 12345), (6, 6141), (7, 7 * 2048 * 3 + 11),
           (8, 8 * 4096 * 2), (8, 8 * 4096 * 2 + 5), (8, 5), (8, 25), (8, 7 * 4096 + 4093), (9, 100_003),
-          (16, 16 * 1000), (33, 33 * 257 + 1), (64, 64 * 1024)]
+          (12, 12 * 3001 + 5), (16, 16 * 1000), (33, 33 * 257 + 1), (64, 64 * 1024)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
