@@ -18,11 +18,12 @@
 //     grid-wide barrier between steps (the per-step synchronisation of a real
 //     ring).
 //
-// Both stream 16-byte vectors when every chunk starts on a 16-byte boundary
-// (L a multiple of the elements per vector and 16-byte aligned buffers), and
-// fall back to one element per thread otherwise. A block works on tiles that
-// never cross a chunk boundary. No LDS and no matrix cores: nothing here is
-// reused across threads or shaped like a contraction.
+// Both stream 16-byte vectors when the rank buffers are 16-byte aligned, and
+// fall back to one element per thread otherwise. A block works on tiles of
+// one chunk, on a grid aligned to whole tiles of the buffer; a vector that a
+// chunk boundary cuts (chunk lengths that are not whole vectors) is done
+// element by element, this chunk's elements only. No LDS and no matrix
+// cores: nothing here is reused across threads or shaped like a contraction.
 #include <algorithm>
 
 #include "ring_common.h"
@@ -47,6 +48,11 @@ constexpr int kPersistentBlocksPer8CUsStreaming = 6;
 constexpr int kPersistentBlocksPer8CUsCached = 3;
 
 // ---------------------------------------------------------------- one step
+
+// The step kernels stream 16-byte vectors whenever every rank buffer starts
+// on a 16-byte boundary; a vector cut by a chunk boundary (chunk lengths
+// that are not whole vectors) is done element by element.
+inline bool step_vec(const RingArgs& a) { return all_aligned16(const_cast<void* const*>(a.P.p), a.n); }
 
 // Chunk that rank r passes on in step s of `phase`.
 __device__ __forceinline__ int step_chunk(int r, int s, int n, int phase) {
@@ -96,9 +102,11 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
           y = O::to(acc);
         }
         st16<NT>(static_cast<u32x4*>(dst) + vi[u], y);
-      } else if (vi[u] * V >= lo) {
+      } else if ((vi[u] + 1) * V > lo && vi[u] * V < hi) {
+        // A vector cut by a chunk boundary (chunk lengths that are not whole
+        // vectors) or by the end of the buffer: this chunk's elements only.
         const int64_t e0 = vi[u] * V;
-        for (int64_t e = e0; e < hi && e < e0 + V; ++e) {
+        for (int64_t e = max(e0, lo); e < hi && e < e0 + V; ++e) {
           const float x = O::load1(src, e);
           O::store1(dst, e, phase == DDP_RS ? O::add1(x, O::load1(dst, e)) : x);
         }
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
 // Tiles per chunk of the persistent kernel (256 threads x kStepUnroll vectors).
 template <int DT>
 int64_t step_tiles_per_chunk(const RingArgs& a) {
-  const int64_t tile = a.vec ? int64_t(kPersistentThreads) * kStepUnroll * Ops<DT>::V : kPersistentThreads;
+  const int64_t tile = step_vec(a) ? int64_t(kPersistentThreads) * kStepUnroll * Ops<DT>::V : kPersistentThreads;
   return aligned_tiles_per_chunk(a.L, tile);
 }
 
@@ -214,7 +222,7 @@ int launch_step_impl(const RingArgs& a, int step, int phase, hipStream_t s) {
 template <int DT>
 int launch_step(const RingArgs& a, int step, int phase, hipStream_t s) {
   const bool nt = int64_t(a.n) * a.count * elem_bytes(DT) > kCacheResidentBytes;
-  if (a.vec)
+  if (step_vec(a))
     return nt ? launch_step_impl<DT, true, true>(a, step, phase, s) : launch_step_impl<DT, true, false>(a, step, phase, s);
   return nt ? launch_step_impl<DT, false, true>(a, step, phase, s) : launch_step_impl<DT, false, false>(a, step, phase, s);
 }
@@ -299,11 +307,11 @@ int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int3
   hipStream_t s = as_stream(stream);
   const bool nt = int64_t(a.n) * a.count * elem_bytes(dtype) > kCacheResidentBytes;
   if (dtype == DDP_FP32) {
-    if (a.vec) return nt ? launch_persistent_impl<DDP_FP32, true, true>(a, n_steps, o, s)
+    if (step_vec(a)) return nt ? launch_persistent_impl<DDP_FP32, true, true>(a, n_steps, o, s)
                          : launch_persistent_impl<DDP_FP32, true, false>(a, n_steps, o, s);
     return launch_persistent_impl<DDP_FP32, false, false>(a, n_steps, o, s);
   }
-  if (a.vec) return nt ? launch_persistent_impl<DDP_BF16, true, true>(a, n_steps, o, s)
+  if (step_vec(a)) return nt ? launch_persistent_impl<DDP_BF16, true, true>(a, n_steps, o, s)
                        : launch_persistent_impl<DDP_BF16, true, false>(a, n_steps, o, s);
   return launch_persistent_impl<DDP_BF16, false, false>(a, n_steps, o, s);
 }
@@ -343,7 +351,7 @@ extern "C" int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int3
   a.n = N;
   a.count = count;
   a.L = (count + N - 1) / N;
-  a.vec = a.L % (kVectorBytes / elem_bytes(dtype)) == 0;  // assuming 16-byte aligned buffers
+  a.vec = true;  // the step kernels stream vectors whenever the buffers are 16-byte aligned (assumed here)
   unsigned g = 0;
   int cus = 0;
   // the same choice of kernel as the launch: the default grid depends on the cache regime
