@@ -23,7 +23,44 @@ constexpr int kScatterThreads = 64;
 constexpr int kScatterBatch = 16;
 constexpr int64_t kScatterCacheResidentBytes = int64_t(256) << 20;
 
-// NR > 0: compile-time rank count; NR == 0: any N, loaded kScatterBatch at a time.
+// Vector vi of the N ranks summed in ring order from rank `first` (one
+// rounding per add). NR > 0: compile-time rank count; NR == 0: any N, loaded
+// kScatterBatch at a time.
+template <int DT, int NR, bool NTL>
+__device__ __forceinline__ typename Ops<DT>::Acc ring_sum_vec(const RankPtrs& P, int n, int first, int64_t vi) {
+  using O = Ops<DT>;
+  typename O::Acc a;
+  if constexpr (NR > 0) {
+    u32x4 x[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) x[k] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k, NR)]) + vi);
+    a = O::from(x[0]);
+#pragma unroll
+    for (int k = 1; k < NR; ++k) O::add(a, x[k]);
+  } else {
+    a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
+    for (int k = 1; k < n; k += kScatterBatch) {
+      u32x4 x[kScatterBatch];
+#pragma unroll
+      for (int j = 0; j < kScatterBatch; ++j)
+        if (k + j < n) x[j] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
+#pragma unroll
+      for (int j = 0; j < kScatterBatch; ++j)
+        if (k + j < n) O::add(a, x[j]);
+    }
+  }
+  return a;
+}
+
+// Element e of the N ranks summed in ring order from rank `first`, scaled.
+template <int DT>
+__device__ __forceinline__ float ring_sum_elem(const RankPtrs& P, int n, int first, int64_t e, float scale) {
+  using O = Ops<DT>;
+  float acc = O::load1(P.p[first], e);
+  for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
+  return O::mul1(acc, scale);
+}
+
 template <int DT, int NR, bool NTL>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter_vec(RankPtrs P, RankPtrs S, int n_rt, int64_t count,
                                                                  int64_t L, int64_t tiles_per_chunk,
@@ -41,38 +78,51 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter_vec(RankPtrs P, Ran
     const int first = wrap(c + 1, n);
     void* shard = S.p[c];
     if ((vi + 1) * V <= hi) {
-      typename O::Acc a;
-      if constexpr (NR > 0) {
-        u32x4 x[NR];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) x[k] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k, NR)]) + vi);
-        a = O::from(x[0]);
-#pragma unroll
-        for (int k = 1; k < NR; ++k) O::add(a, x[k]);
-      } else {
-        a = O::from(ld16<NTL>(static_cast<const u32x4*>(P.p[first]) + vi));
-        for (int k = 1; k < n; k += kScatterBatch) {
-          u32x4 x[kScatterBatch];
-#pragma unroll
-          for (int j = 0; j < kScatterBatch; ++j)
-            if (k + j < n) x[j] = ld16<NTL>(static_cast<const u32x4*>(P.p[wrap(first + k + j, n)]) + vi);
-#pragma unroll
-          for (int j = 0; j < kScatterBatch; ++j)
-            if (k + j < n) O::add(a, x[j]);
-        }
-      }
+      const typename O::Acc a = ring_sum_vec<DT, NR, NTL>(P, n, first, vi);
       st16<true>(static_cast<u32x4*>(shard) + (vi - lo / V), O::scale(O::to(a), scale));
     } else {
-      for (int64_t e = vi * V; e < hi; ++e) {
-        float acc = O::load1(P.p[first], e);
-        for (int k = 1; k < n; ++k) acc = O::add1(acc, O::load1(P.p[wrap(first + k, n)], e));
-        O::store1(shard, e - lo, O::mul1(acc, scale));
+      for (int64_t e = vi * V; e < hi; ++e) O::store1(shard, e - lo, ring_sum_elem<DT>(P, n, first, e, scale));
+    }
+  }
+}
+
+// Chunk lengths that are not whole vectors: tiles run over the whole buffer
+// from its 16-byte aligned start, so the loads stay 16-byte vectors. A
+// vector inside one chunk is summed as a vector and written to the shard
+// element by element (the shard's elements do not line up with the buffer's
+// vectors); a vector cut by a chunk boundary or by the end of the buffer is
+// done element by element, each element in its own chunk's order. A tile is
+// never longer than a chunk here, so it crosses at most one boundary.
+template <int DT, int NR, bool NTL>
+__global__ __launch_bounds__(kScatterThreads) void k_scatter_any(RankPtrs P, RankPtrs S, int n_rt, int64_t count,
+                                                                 int64_t L, int64_t total_tiles, float scale) {
+  using O = Ops<DT>;
+  constexpr int V = O::V;
+  const int n = NR > 0 ? NR : n_rt;
+  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    const int64_t tile_e = tile * kScatterThreads * V;
+    const int64_t c0 = tile_e / L;  // chunk of the tile's first element
+    const int64_t next = (c0 + 1) * L;
+    const int64_t vi = tile * kScatterThreads + threadIdx.x;
+    const int64_t e0 = vi * V;
+    if (e0 >= count) continue;
+    const int c = int(c0) + (e0 >= next ? 1 : 0);
+    const int64_t lo = int64_t(c) * L;
+    if (e0 + V <= min(lo + L, count)) {
+      const typename O::Acc a = ring_sum_vec<DT, NR, NTL>(P, n, wrap(c + 1, n), vi);
+      const u32x4 y = O::scale(O::to(a), scale);
+      for (int j = 0; j < V; ++j) O::store1(S.p[c], e0 - lo + j, Word<DT>::elem(y, j));
+    } else {
+      for (int64_t e = e0; e < e0 + V && e < count; ++e) {
+        const int ce = int(c0) + (e >= next ? 1 : 0);
+        O::store1(S.p[ce], e - int64_t(ce) * L, ring_sum_elem<DT>(P, n, wrap(ce + 1, n), e, scale));
       }
     }
   }
 }
 
-// Fallback for chunks that do not start on 16-byte boundaries: one element per thread.
+// Fallback for unaligned buffers and for chunks shorter than a tile whose
+// length is not a whole number of vectors: one element per thread.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_scatter_scalar(RankPtrs P, RankPtrs S, int n, int64_t count, int64_t L,
                                                              int64_t tiles_per_chunk, int64_t total_tiles,
@@ -116,13 +166,44 @@ void launch_scatter_vec(const RingArgs& a, const RankPtrs& S, float scale, hipSt
   }
 }
 
+template <int DT, bool NTL>
+void launch_scatter_any(const RingArgs& a, const RankPtrs& S, float scale, hipStream_t s) {
+  constexpr int V = Ops<DT>::V;
+  const int64_t total = (a.count + int64_t(kScatterThreads) * V - 1) / (int64_t(kScatterThreads) * V);
+  const dim3 g(grid_for(total)), b(kScatterThreads);
+  switch (a.n) {
+#define DDP_SCATTER_ANY_CASE(NR)                                                                           \
+  case NR:                                                                                                 \
+    hipLaunchKernelGGL((k_scatter_any<DT, NR, NTL>), g, b, 0, s, a.P, S, a.n, a.count, a.L, total, scale); \
+    break;
+    DDP_SCATTER_ANY_CASE(1)
+    DDP_SCATTER_ANY_CASE(2)
+    DDP_SCATTER_ANY_CASE(3)
+    DDP_SCATTER_ANY_CASE(4)
+    DDP_SCATTER_ANY_CASE(5)
+    DDP_SCATTER_ANY_CASE(6)
+    DDP_SCATTER_ANY_CASE(7)
+    DDP_SCATTER_ANY_CASE(8)
+#undef DDP_SCATTER_ANY_CASE
+    default:
+      hipLaunchKernelGGL((k_scatter_any<DT, 0, NTL>), g, b, 0, s, a.P, S, a.n, a.count, a.L, total, scale);
+  }
+}
+
 template <int DT>
 int launch_scatter(const RingArgs& a, const RankPtrs& S, bool shards_aligned, float scale, hipStream_t s) {
+  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kScatterCacheResidentBytes;
   if (a.vec && shards_aligned) {
-    if (int64_t(a.n) * a.count * elem_bytes(DT) > kScatterCacheResidentBytes)
+    if (ntl)
       launch_scatter_vec<DT, true>(a, S, scale, s);
     else
       launch_scatter_vec<DT, false>(a, S, scale, s);
+  } else if (all_aligned16(const_cast<void* const*>(a.P.p), a.n) &&
+             a.L >= int64_t(kScatterThreads) * Ops<DT>::V) {
+    if (ntl)
+      launch_scatter_any<DT, true>(a, S, scale, s);
+    else
+      launch_scatter_any<DT, false>(a, S, scale, s);
   } else {
     const int64_t tpc = (a.L + kThreads - 1) / kThreads;
     const int64_t total = tpc * a.n;
