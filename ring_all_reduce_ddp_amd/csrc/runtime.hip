@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void k_count_mismatch(RankPtrs P, int n, 
   partial[threadIdx.x] = local;
   __syncthreads();
   for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) partial[threadIdx.x] += partial[threadIdx.x + w];
+    if (int(threadIdx.x) < w) partial[threadIdx.x] += partial[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0 && partial[0] != 0) atomicAdd(out, partial[0]);
