@@ -49,7 +49,6 @@ extern "C" int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, in
 extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params, int32_t grad_dtype,
                                   int32_t comm_dtype, int64_t cap_bytes, int64_t first_bucket_bytes,
                                   int32_t world_size, ddp_plan** out) {
-  const int32_t dtype = grad_dtype;
   if (out == nullptr) return fail(DDP_EINVAL, "ddp_bucket_plan: out is NULL");
   *out = nullptr;
   if (n_params < 0) return fail(DDP_EINVAL, "ddp_bucket_plan: n_params < 0");
