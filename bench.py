@@ -8,10 +8,13 @@ all-reduce), algorithm bandwidth S / t, and the HBM bandwidth of the kernel,
 2 * N * S / t, against MI355X's 8 TB/s.
 
 Beside it, in the same run: the step-by-step and persistent forms, the
-reduce-scatter output alone, and the bf16 buffers of the same workload, one
-default-size DDP bucket (8 x 25 MiB, cache-resident) in all three forms, a
-copy probe, the whole DDP sync of ResNet-50 gradients (8 ranks; copying,
-in-place and bf16-compressed), the overlap of that sync with a synthetic
+reduce-scatter output alone, the same inputs in one allocation with the ranks
+offset by 4 KiB, and the bf16 buffers of the same workload, the
+launch cost of the pages' 3-rank example, one default-size DDP bucket
+(8 x 25 MiB, cache-resident, and again with the cache flushed before each
+launch) in all three forms, a copy probe, the whole DDP sync of ResNet-50
+gradients (8 ranks; copying, kernel by kernel, in-place and bf16-compressed),
+the overlap of that sync with a synthetic
 backward over bucket capacities, the 64-rank 300M-element workload, and the
 CPU oracle timed on the headline workload's own inputs.
 
@@ -65,6 +68,23 @@ def time_launches(fn, reps, torch):
     return start.elapsed_time(end) / reps
 
 
+def time_each(fn, reps, torch, between=None):
+    """Milliseconds of each of `reps` calls of fn(), each bracketed by its own
+    pair of HIP events on torch's current stream; `between()`, if given, runs
+    before every call, outside the timed pair. Returns (mean, median, min)."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        if between is not None:
+            between()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    return sum(t) / reps, t[reps // 2] if reps % 2 else 0.5 * (t[reps // 2 - 1] + t[reps // 2]), t[0]
+
+
 def gbps(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
@@ -95,7 +115,7 @@ def main():
     import numpy as np
     import torch
     import ring_all_reduce_ddp_amd as rar
-    from ddp_workloads import WORKLOADS, device_ring_inputs, resnet50_param_numels
+    from ddp_workloads import WORKLOADS, device_ring_inputs, host_ring_inputs, resnet50_param_numels
 
     torch.cuda.set_device(0)
 
@@ -112,6 +132,8 @@ def main():
         rar.ring_allreduce_fused(bufs)
     torch.cuda.synchronize()
     ms = time_launches(lambda: rar.ring_allreduce_fused(bufs), args.steps, torch)
+    # the same launches one by one, for the median and the fastest
+    _, ms_median, ms_min = time_each(lambda: rar.ring_allreduce_fused(bufs), args.steps, torch)
     mism = torch.zeros(1, dtype=torch.int64, device="cuda")
     rar.ddp_count_mismatches(bufs, mism)
     torch.cuda.synchronize()
@@ -153,6 +175,29 @@ def main():
     del bufs, shards
     torch.cuda.empty_cache()
 
+    # Layout study: the same kernel on the same inputs with the 8 rank buffers
+    # carved from one allocation, rank r at byte r * (S + 4 KiB). Separate
+    # 1 GiB allocations start 2 MiB apart, so every block's 8 loads of one
+    # offset agree in their low 21 address bits; offsets between the ranks
+    # that are not multiples of 8 KiB ran faster at this size (multiples of
+    # 8 KiB did not), which points at DRAM bank conflicts. Reported beside
+    # the headline, which keeps the separate allocations a caller would
+    # normally hand over.
+    pad = 4096 // 4
+    arena = torch.empty(n * (count + pad), device="cuda")
+    views = [arena[r * (count + pad): r * (count + pad) + count] for r in range(n)]
+    for r, src in enumerate(device_ring_inputs(w.seed, n, count, "fp32", std=w.std)):
+        views[r].copy_(src)
+        del src
+    rar.ring_allreduce_fused(views)
+    t = time_launches(lambda: rar.ring_allreduce_fused(views), reps, torch)
+    extras["layout_one_allocation_4kib_offset"] = {
+        "ms": round(t, 4), "hbm_gbps": round(gbps(2 * n * S, t), 1),
+        "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4),
+        "rank_stride_bytes": (count + pad) * 4}
+    del arena, views
+    torch.cuda.empty_cache()
+
     bb = device_ring_inputs(w.seed, n, 2 * count, "bf16", std=w.std)
     rar.ring_allreduce_fused(bb)
     t = time_launches(lambda: rar.ring_allreduce_fused(bb), reps, torch)
@@ -161,6 +206,26 @@ def main():
                             "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4)}
     del bb
     torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ 3 ranks x 6 elements: launch cost
+    # The four-step example of the pages: latency only (72 bytes in all), so
+    # the figure is the time per call as issued from Python, and the kernel
+    # time alone from one event pair per call.
+    w1 = WORKLOADS["ring_n3_6"]
+    b1 = [torch.from_numpy(x).cuda() for x in host_ring_inputs(w1.seed, w1.n, w1.count, "fp32", dist=w1.dist)]
+    tiny = {"ranks": w1.n, "elements_per_rank": w1.count}
+    for name, fn in (("step", lambda: rar.ring_allreduce_step(b1, 0, rar.DDP_RS)),
+                     ("steps_all", lambda: rar.ring_allreduce_stepwise(b1)),
+                     ("persistent", lambda: rar.ring_allreduce_persistent(b1)),
+                     ("fused", lambda: rar.ring_allreduce_fused(b1))):
+        fn()
+        per_call = time_launches(fn, 1000, torch)
+        _, med, lo = time_each(fn, 200, torch)
+        tiny[name] = {"us_per_call_back_to_back": round(per_call * 1e3, 2),
+                      "us_gpu_median": round(med * 1e3, 2), "us_gpu_min": round(lo * 1e3, 2)}
+    rar.ddp_persistent_status()
+    extras["ring_n3_6"] = tiny
+    del b1
 
     # ------------------------------------------------------------ one default-size DDP bucket
     # 8 ranks x 25 MiB fp32 (6,553,600 elements): 200 MiB in all, inside the
@@ -177,6 +242,17 @@ def main():
         bucket[name] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, t), 1),
                         "algorithm_gbps": round(gbps(S2, t), 1), "hbm_gbps": round(gbps(nbytes, t), 1)}
     rar.ddp_persistent_status()
+    # the same bucket with the Infinity Cache flushed before each launch by
+    # writing a 512 MiB buffer (outside the timed region): HBM-resident inputs
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = {}
+    for name, fn in (("fused", lambda: rar.ring_allreduce_fused(b2)),
+                     ("steps", lambda: rar.ring_allreduce_stepwise(b2))):
+        mean, med, lo = time_each(fn, 20, torch, between=flush.zero_)
+        cold[name] = {"ms_median": round(med, 4), "ms_min": round(lo, 4),
+                      "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, med), 1)}
+    bucket["after_cache_flush"] = cold
+    del flush
     extras["ring_n8_25mib"] = bucket
     del b2
     torch.cuda.empty_cache()
@@ -216,6 +292,20 @@ def main():
             # pack + fused + unpack move 6*N*S; the in-place sync 2*N*S (padding excluded)
             sync_bytes = (2 if variant == "view" else 6) * wr.n * grad_bytes
             sync[variant]["hbm_gbps_algorithmic"] = round(gbps(sync_bytes, t), 1)
+    # the copying sync kernel by kernel: all packs, all fused all-reduces, all unpacks
+    nb = plan.num_buckets
+    parts = {
+        "pack": lambda: [rar.bucket_pack(plan, b, arenas, buckets[b]) for b in range(nb)],
+        "allreduce_fused": lambda: [rar.ring_allreduce_fused(buckets[b]) for b in range(nb)],
+        "unpack_scale": lambda: [rar.bucket_unpack_scale(plan, b, buckets[b], arenas, 1.0 / wr.n)
+                                 for b in range(nb)],
+    }
+    breakdown = {}
+    for name, fn in parts.items():
+        fn()
+        t = time_launches(fn, reps, torch)
+        breakdown[name] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
+    sync["fused"]["breakdown"] = breakdown
     # the bf16 compression hook: fp32 gradients through bf16 buckets
     cplan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=wr.n)
     cbuckets = [[torch.empty(cplan.bucket(b)[0], dtype=torch.bfloat16, device="cuda") for _ in range(wr.n)]
@@ -309,7 +399,10 @@ def main():
         "config": {"workload": "ring_n8_1gib", "virtual_ranks": n, "elements_per_rank": count,
                    "bytes_per_rank": S, "variant": "fused", "in_place": True},
         "algbw_gbps": round(gbps(S, ms), 2), "busbw_gbps": round(bus, 2), "hbm_gbps": round(hbm, 1),
-        "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4), "ranks_equal_after": ranks_equal,
+        "hbm_frac_of_peak": round(hbm / PEAK_HBM_GBPS, 4),
+        "hbm_frac_of_copy_probe": round(hbm / extras["copy_probe"]["gbps"], 4),
+        "ms_per_launch_median": round(ms_median, 4), "ms_per_launch_min": round(ms_min, 4),
+        "ranks_equal_after": ranks_equal,
         "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": hbm_bytes},
