@@ -104,8 +104,13 @@ def oracle_sync(grads, numels, n, dtype="fp32"):
 ALL_VARIANTS = ["fused", "steps", "persistent", "view"]
 
 
-def sync_case(variant, n, dtype, numels, cap, first, seed, scale=None):
-    plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+def sync_case(variant, n, dtype, numels, cap, first, seed, scale=None, comm=None):
+    """One sync on seeded gradients against the oracle's; comm="bf16" with
+    fp32 gradients goes through bf16 buckets (the compression hook)."""
+    if comm is None:
+        plan = rar.ddp_bucket_plan(numels, dtype, cap_bytes=cap, first_bucket_bytes=first, world_size=n)
+    else:
+        plan = rar.ddp_bucket_plan_ex(numels, dtype, comm, cap, first, n)
     grads = host_grads(seed, n, numels)
     if dtype == "bf16":
         from ddp_workloads.gen import to_bf16_bits
@@ -114,14 +119,17 @@ def sync_case(variant, n, dtype, numels, cap, first, seed, scale=None):
     else:
         grads_f32 = grads
     arenas, offs = make_arenas(plan, grads_f32, dtype)
-    buckets = None if variant == "view" else bucket_buffers(plan, n, dtype)
+    buckets = None if variant == "view" else bucket_buffers(plan, n, comm or dtype)
     rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=scale)
     torch.cuda.synchronize()
     if variant == "persistent":
         rar.ddp_persistent_status()
     got = read_grads(arenas, offs, numels, dtype)
-    oplan = planner.plan(numels, 4 if dtype == "fp32" else 2, cap, first, n)
-    want = ddp.ddp_sync(grads, oplan, dtype, scale=scale)
+    if comm is None:
+        oplan = planner.plan(numels, 4 if dtype == "fp32" else 2, cap, first, n)
+    else:
+        oplan = planner.plan(numels, 4, cap, first, n, vector_elems=8)
+    want = ddp.ddp_sync(grads, oplan, dtype, scale=scale, comm_dtype=comm)
     for r in range(n):
         for p in range(len(numels)):
             assert_bit_equal(got[r][p], want[r][p], f"{variant} n={n} {dtype} rank {r} param {p}")
