@@ -11,6 +11,11 @@
 namespace ddp {
 
 constexpr int kVectorBytes = 16;
+// MI355X's Infinity Cache (the memory-side last-level cache). Kernels whose
+// buffers together exceed it stream them with non-temporal loads and stores;
+// below it they use cached accesses, so data written by one kernel is read
+// from the cache by the next.
+constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;
 
 inline int elem_bytes(int32_t dtype) { return dtype == DDP_BF16 ? 2 : 4; }
 inline bool valid_dtype(int32_t dtype) { return dtype == DDP_FP32 || dtype == DDP_BF16; }

@@ -34,7 +34,6 @@ namespace {
 
 constexpr int kFusedThreads = 64;   // threads per wave and vectors per rank tile
 constexpr int kFusedMaxWaves = 8;
-constexpr int64_t kFusedCacheResidentBytes = int64_t(256) << 20;
 
 // LDS for one tile of every rank: a fixed array for a compile-time rank
 // count, else the launch's dynamic LDS (N KiB).
@@ -270,7 +269,7 @@ void launch_fused_any(const RingArgs& a, hipStream_t s) {
 
 template <int DT>
 int launch_fused(const RingArgs& a, hipStream_t s) {
-  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kFusedCacheResidentBytes;
+  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kInfinityCacheBytes;
   if (a.vec) {
     if (ntl)
       launch_fused_vec<DT, true>(a, s);

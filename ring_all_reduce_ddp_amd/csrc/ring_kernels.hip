@@ -128,7 +128,6 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
 // they fit, cached accesses let step s+1 read what step s wrote from the cache
 // (8 x 25 MiB: 0.15 ms vs 0.18 ms non-temporal).
 constexpr int kStepThreads = 64;
-constexpr int64_t kCacheResidentBytes = int64_t(256) << 20;
 
 template <int DT, bool VEC, int PHASE, bool NT>
 __global__ __launch_bounds__(kStepThreads) void k_step(RankPtrs P, int n, int64_t count, int64_t L,
@@ -221,7 +220,7 @@ int launch_step_impl(const RingArgs& a, int step, int phase, hipStream_t s) {
 
 template <int DT>
 int launch_step(const RingArgs& a, int step, int phase, hipStream_t s) {
-  const bool nt = int64_t(a.n) * a.count * elem_bytes(DT) > kCacheResidentBytes;
+  const bool nt = int64_t(a.n) * a.count * elem_bytes(DT) > kInfinityCacheBytes;
   if (step_vec(a))
     return nt ? launch_step_impl<DT, true, true>(a, step, phase, s) : launch_step_impl<DT, true, false>(a, step, phase, s);
   return nt ? launch_step_impl<DT, false, true>(a, step, phase, s) : launch_step_impl<DT, false, false>(a, step, phase, s);
@@ -305,7 +304,7 @@ int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int3
   if (st != DDP_OK) return st;
   if (count == 0 || n_steps == 0) return DDP_OK;
   hipStream_t s = as_stream(stream);
-  const bool nt = int64_t(a.n) * a.count * elem_bytes(dtype) > kCacheResidentBytes;
+  const bool nt = int64_t(a.n) * a.count * elem_bytes(dtype) > kInfinityCacheBytes;
   if (dtype == DDP_FP32) {
     if (step_vec(a)) return nt ? launch_persistent_impl<DDP_FP32, true, true>(a, n_steps, o, s)
                          : launch_persistent_impl<DDP_FP32, true, false>(a, n_steps, o, s);
@@ -355,7 +354,7 @@ extern "C" int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int3
   unsigned g = 0;
   int cus = 0;
   // the same choice of kernel as the launch: the default grid depends on the cache regime
-  const bool nt = a.vec && int64_t(N) * count * elem_bytes(dtype) > kCacheResidentBytes;
+  const bool nt = a.vec && int64_t(N) * count * elem_bytes(dtype) > kInfinityCacheBytes;
   int st;
   if (dtype == DDP_FP32)
     st = !a.vec ? persistent_grid<DDP_FP32, false, false>(a, 0, &g, &cus)

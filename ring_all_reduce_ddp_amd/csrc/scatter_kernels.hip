@@ -21,7 +21,6 @@ namespace {
 
 constexpr int kScatterThreads = 64;
 constexpr int kScatterBatch = 16;
-constexpr int64_t kScatterCacheResidentBytes = int64_t(256) << 20;
 
 // Vector vi of the N ranks summed in ring order from rank `first` (one
 // rounding per add). NR > 0: compile-time rank count; NR == 0: any N, loaded
@@ -192,7 +191,7 @@ void launch_scatter_any(const RingArgs& a, const RankPtrs& S, float scale, hipSt
 
 template <int DT>
 int launch_scatter(const RingArgs& a, const RankPtrs& S, bool shards_aligned, float scale, hipStream_t s) {
-  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kScatterCacheResidentBytes;
+  const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kInfinityCacheBytes;
   if (a.vec && shards_aligned) {
     if (ntl)
       launch_scatter_vec<DT, true>(a, S, scale, s);

@@ -38,7 +38,6 @@
 namespace ddp {
 namespace {
 
-constexpr int64_t kViewCacheResidentBytes = int64_t(256) << 20;
 constexpr int kViewMaxWaves = 8;  // waves per block (one rank each, or every 8th rank when N > 8)
 
 // One tile of the in-place sync: arena vectors [64 * tile, 64 * tile + 64),
@@ -190,7 +189,7 @@ int launch_view_bucket(const ddp_plan* plan, int32_t b, const RankPtrs& P, int32
   const int eb = elem_bytes(plan->dtype);
   // Buckets are reduced one after the other over the whole arena, so the
   // arena's size, not one bucket's, decides whether loads can hit the cache.
-  const bool ntl = int64_t(N) * plan->arena_numel * eb > kViewCacheResidentBytes;
+  const bool ntl = int64_t(N) * plan->arena_numel * eb > kInfinityCacheBytes;
   const ViewSpan sp{info, bk.view_vec_begin / kViewThreads, bk.n_view_tiles, bk.view_vec_begin, bk.view_vec_end};
   if (plan->dtype == DDP_FP32) {
     if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, max_blocks, s);
@@ -210,7 +209,7 @@ int launch_view_arena(const ddp_plan* plan, const RankPtrs& P, int32_t N, float 
   int st = device_tables(const_cast<ddp_plan*>(plan), nullptr, &info);
   if (st != DDP_OK) return st;
   const int eb = elem_bytes(plan->dtype);
-  const bool ntl = int64_t(N) * plan->arena_numel * eb > kViewCacheResidentBytes;
+  const bool ntl = int64_t(N) * plan->arena_numel * eb > kInfinityCacheBytes;
   const ViewSpan sp{info, 0, (vecs + kViewThreads - 1) / kViewThreads, 0, vecs};
   if (plan->dtype == DDP_FP32) {
     if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, 0, s);

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import ring_all_reduce_ddp_amd as rar
-from oracle import ddp, planner
+from oracle import ddp, planner, ring
 from ddp_workloads import WORKLOADS, host_grads, resnet50_param_numels
 
 from gpu_util import TORCH_DTYPE, to_host, assert_bit_equal
@@ -318,3 +318,65 @@ def test_view_bucket_by_bucket(dtype, n, order):
     for r in range(n):
         for p in range(len(numels)):
             assert_bit_equal(got[r][p], want[r][p], f"n={n} {dtype} rank {r} param {p}")
+
+
+def bucket_space_samples(oplan, offs, n, k, seed):
+    """Arena positions to check, drawn in bucket space: the first two and last
+    two offsets of every ring chunk of every bucket plus k random offsets, kept
+    where they fall inside a member. Returns (arena indices, chunk ids)."""
+    rng = np.random.default_rng(seed)
+    idx, chunk = [], []
+    for bk in oplan:
+        padded = bk["padded_numel"]
+        L = padded // n
+        cand = [rng.integers(0, padded, size=k // len(oplan) + 1)]
+        for c in range(n):
+            cand.append(np.array([c * L, c * L + 1, (c + 1) * L - 2, (c + 1) * L - 1]))
+        cand = np.unique(np.concatenate(cand))
+        for p, off, numel in bk["members"]:
+            inside = cand[(cand >= off) & (cand < off + numel)]
+            idx.append(offs[p] + inside - off)
+            chunk.append(inside // L)
+    return np.concatenate(idx).astype(np.int64), np.concatenate(chunk).astype(np.int64)
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+def test_bf16_resnet50_sampled(variant):
+    """bf16 gradients of ResNet-50 over 8 ranks (409 MB of arenas, beyond the
+    Infinity Cache, so pack and unpack stream): sampled positions against the
+    oracle's ring on those positions, in their chunks' order, then its
+    unpack_scale; all ranks equal everywhere."""
+    w = WORKLOADS["ddp_resnet50"]
+    n = w.n
+    numels = resnet50_param_numels()
+    plan = rar.ddp_bucket_plan(numels, "bf16", world_size=n)
+    arena_numel, offs = plan.grad_arena()
+    oplan = planner.plan(numels, 2, world_size=n)
+    mask = torch.zeros(arena_numel, dtype=torch.bool, device="cuda")
+    for p, m in enumerate(numels):
+        mask[offs[p]:offs[p] + m] = True
+    g = torch.Generator(device="cuda")
+    arenas = []
+    for r in range(n):
+        g.manual_seed(1000 * w.seed + 500 + r)
+        a = (torch.randn(arena_numel, generator=g, device="cuda") * w.std).to(torch.bfloat16)
+        arenas.append(torch.where(mask, a, torch.zeros_like(a)))  # slack is zero, as a fresh arena's
+    pos, chunk = bucket_space_samples(oplan, offs, n, 20000, seed=7)
+    pos_dev = torch.from_numpy(pos).cuda()
+    before = [to_host(a.index_select(0, pos_dev), "bf16") for a in arenas]
+    print(f"[resnet50 bf16 {variant}] arena={arena_numel} samples={len(pos)}", flush=True)
+    buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
+    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+    torch.cuda.synchronize()
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+    after = [to_host(a.index_select(0, pos_dev), "bf16") for a in arenas]
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rar.ddp_count_mismatches(arenas, mism)
+    torch.cuda.synchronize()
+    assert int(mism.item()) == 0, "ranks differ after the sync"
+    reduced = ring.ring_simulate(before, "bf16", chunk_of=chunk)["bufs"][0]
+    flat = {"members": [(0, 0, len(pos))], "padded_numel": len(pos)}
+    want = ddp.unpack_scale(reduced, flat, np.float32(1) / np.float32(n), "bf16")[0]
+    for r in range(n):
+        assert_bit_equal(after[r], want, f"{variant} rank {r}")
