@@ -111,6 +111,58 @@ __global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_staged
   }
 }
 
+// Buffers cut into N equal chunks of whole tiles (count = N * L, L a multiple
+// of 64 vectors: 8 x 1 GiB, one 8 x 25 MiB bucket): every tile lies inside
+// its chunk, so nothing is bounds-checked, and each rank's tile is staged in
+// the LDS row of its place in the chunk's ring order (rank c+1 in row 0, rank
+// c+2 in row 1, ...), so the sum reads rows 0, 1, ..., N-1 at fixed offsets.
+// The additions and their order are those of k_fused_staged; the lighter
+// index work before the loads measured 6.55 against 6.47 TB/s at 8 x 1 GiB
+// fp32 in a stand-alone copy of the same access pattern.
+template <int DT, int NR, bool NTL>
+__global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_whole(RankPtrs P, int n_rt,
+                                                                              int64_t tiles_per_chunk, int64_t t0) {
+  using Wd = Word<DT>;
+  constexpr int W = NR > 0 ? NR : kFusedMaxWaves;
+  constexpr int kSlots = NR > 0 ? 1 : DDP_MAX_RANKS / kFusedMaxWaves;
+  constexpr int kWords = kFusedThreads * 4;
+  u32x4* stage = staged_tile<NR>();
+  const int n = NR > 0 ? NR : n_rt;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kFusedThreads);
+  const int lane = int(threadIdx.x) % kFusedThreads;
+  const int c = int(blockIdx.y);
+  const int first = wrap(c + 1, n);  // the chunk's ring order starts at rank c+1
+  const int64_t vi = (int64_t(c) * tiles_per_chunk + t0 + blockIdx.x) * kFusedThreads + lane;
+  if constexpr (NR > 0) {
+    // One wave per rank: wave w is rank w.
+    u32x4* buf = static_cast<u32x4*>(P.p[wave]);
+    stage[wrap(wave + NR - first, NR) * kFusedThreads + lane] = ld16<NTL>(buf + vi);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int r = wave + j * W;
+      if (r < n)
+        stage[wrap(r + n - first, n) * kFusedThreads + lane] = ld16<NTL>(static_cast<const u32x4*>(P.p[r]) + vi);
+    }
+  }
+  __syncthreads();
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(stage);
+  uint32_t* result = reinterpret_cast<uint32_t*>(stage);
+  for (int d = threadIdx.x; d < kWords; d += W * kFusedThreads)
+    result[d] = Wd::out(ring_sum_rows<DT, NR>(words, kWords, 0, n, d));
+  __syncthreads();
+  const u32x4 y = stage[lane];
+  if constexpr (NR > 0) {
+    st16<true>(static_cast<u32x4*>(P.p[wave]) + vi, y);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int r = wave + j * W;
+      if (r < n) st16<true>(static_cast<u32x4*>(P.p[r]) + vi, y);
+    }
+  }
+}
+
 // Chunk lengths that are not whole 16-byte vectors (an all-reduce of any
 // count; DDP buckets are padded and never need this): the tiles run over the
 // whole buffer from its 16-byte aligned start, so loads and stores stay
@@ -241,6 +293,31 @@ void launch_fused_vec(const RingArgs& a, hipStream_t s) {
 }
 
 template <int DT, bool NTL>
+void launch_fused_whole(const RingArgs& a, hipStream_t s) {
+  const int64_t tpc = a.L / (int64_t(kFusedThreads) * Ops<DT>::V);
+  for (int64_t t0 = 0; t0 < tpc; t0 += kMaxGrid) {
+    const dim3 g(unsigned(std::min(tpc - t0, kMaxGrid)), unsigned(a.n));
+    switch (a.n) {
+#define DDP_FUSED_WHOLE_CASE(NR)                                                                            \
+  case NR:                                                                                                  \
+    hipLaunchKernelGGL((k_fused_whole<DT, NR, NTL>), g, dim3(kFusedThreads * NR), 0, s, a.P, a.n, tpc, t0); \
+    break;
+      DDP_FUSED_WHOLE_CASE(2)
+      DDP_FUSED_WHOLE_CASE(3)
+      DDP_FUSED_WHOLE_CASE(4)
+      DDP_FUSED_WHOLE_CASE(5)
+      DDP_FUSED_WHOLE_CASE(6)
+      DDP_FUSED_WHOLE_CASE(7)
+      DDP_FUSED_WHOLE_CASE(8)
+#undef DDP_FUSED_WHOLE_CASE
+      default:
+        hipLaunchKernelGGL((k_fused_whole<DT, 0, NTL>), g, dim3(kFusedThreads * kFusedMaxWaves),
+                           size_t(a.n) * kFusedThreads * sizeof(u32x4), s, a.P, a.n, tpc, t0);
+    }
+  }
+}
+
+template <int DT, bool NTL>
 void launch_fused_any(const RingArgs& a, hipStream_t s) {
   constexpr int V = Ops<DT>::V;
   const int64_t tiles = (a.count + int64_t(kFusedThreads) * V - 1) / (int64_t(kFusedThreads) * V);
@@ -270,7 +347,13 @@ void launch_fused_any(const RingArgs& a, hipStream_t s) {
 template <int DT>
 int launch_fused(const RingArgs& a, hipStream_t s) {
   const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kInfinityCacheBytes;
-  if (a.vec) {
+  const int64_t tile = int64_t(kFusedThreads) * Ops<DT>::V;
+  if (a.vec && a.count == int64_t(a.n) * a.L && a.L % tile == 0) {
+    if (ntl)
+      launch_fused_whole<DT, true>(a, s);
+    else
+      launch_fused_whole<DT, false>(a, s);
+  } else if (a.vec) {
     if (ntl)
       launch_fused_vec<DT, true>(a, s);
     else

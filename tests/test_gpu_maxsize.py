@@ -26,9 +26,12 @@ def with_edges(pos, count, splits):
     return np.unique(pos[(pos >= 0) & (pos < count)])
 
 
-def test_fused_all_reduce_split_over_launches():
+@pytest.mark.parametrize("extra", [4096, 4092])
+def test_fused_all_reduce_split_over_launches(extra):
+    """One chunk needs two launches; with extra = 4096 the chunks are whole
+    tiles (the whole-tile kernel), with 4092 they end in a partial tile."""
     n = 2
-    L = MAX_GRID_TILES * TILE_FP32 + 4096   # one chunk needs two launches
+    L = MAX_GRID_TILES * TILE_FP32 + extra
     count = n * L
     bufs = device_ring_inputs(31, n, count, "fp32", std=1e-3)
     pos = with_edges(sample_positions(count, n, 20000, seed=31), count,
