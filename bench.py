@@ -13,7 +13,8 @@ offset by 4 KiB, and the bf16 buffers of the same workload, the
 launch cost of the pages' 3-rank example, one default-size DDP bucket
 (8 x 25 MiB, cache-resident, and again with the cache flushed before each
 launch) in all three forms, a copy probe, the whole DDP sync of ResNet-50
-gradients (8 ranks; copying, kernel by kernel, in-place and bf16-compressed),
+gradients (8 ranks; copying, kernel by kernel, in-place, and bf16-compressed
+both ways),
 the overlap of that sync with a synthetic
 backward over bucket capacities, the 64-rank 300M-element workload, and the
 CPU oracle timed on the headline workload's own inputs.
@@ -314,6 +315,12 @@ def main():
     t = time_launches(lambda: rar.ddp_sync(cplan, arenas, cbuckets, variant="fused"), reps, torch)
     sync["bf16_compressed_fused"] = {"ms": round(t, 4),
                                      "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
+    # the same hook in place: bf16 arithmetic on the fp32 gradients, no bf16 bucket (reads and writes 2*N*S)
+    rar.ddp_sync(cplan, arenas, None, variant="view")
+    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, None, variant="view"), reps, torch)
+    sync["bf16_compressed_view"] = {"ms": round(t, 4),
+                                    "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1),
+                                    "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
     extras["ddp_sync_resnet50_n8"] = sync
     del buckets, cbuckets
     torch.cuda.empty_cache()

@@ -118,7 +118,8 @@ int ddp_bucket_plan(const int64_t* param_numels, int32_t n_params, int32_t dtype
  * Communication Hooks"), in which bucket_pack rounds every gradient to bf16
  * (nearest, ties to even), the ring adds in bf16 with one rounding per hop,
  * and bucket_unpack_scale widens to fp32 and rounds scale * value once. The
- * in-place sync (bucket_allreduce_view) needs equal dtypes. */
+ * in-place sync (bucket_allreduce_view) does the same arithmetic on the fp32
+ * gradients themselves. */
 int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params, int32_t grad_dtype,
                        int32_t comm_dtype, int64_t cap_bytes, int64_t first_bucket_bytes,
                        int32_t world_size, ddp_plan** out);
@@ -151,7 +152,9 @@ int ddp_plan_grad_arena(const ddp_plan* plan, int64_t* arena_numel, int64_t* par
  * bucket that holds the vector (low byte) and how many of its V elements
  * belong to the member (high byte, V except in a member's last vector). The
  * kernels read the device copy of this map; the accessor lets the layout be
- * checked on the host. DDP_EINVAL for plans with buckets of another dtype. */
+ * checked on the host. With fp32 gradients in bf16 buckets the entries
+ * describe the fp32 arena (V = 4) and the chunks come from the bf16 buckets'
+ * layout; no arena vector spans two chunks. */
 int ddp_plan_arena_map(const ddp_plan* plan, uint16_t* out, int64_t n);
 
 /* ---------------------------------------------------------------- pack / unpack
@@ -247,7 +250,11 @@ int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dt
  * the sum is multiplied by `scale` (one rounding) and written to every rank's
  * gradient. The result equals bucket_pack + ring_allreduce_fused +
  * bucket_unpack_scale bit for bit, with 2*N*S_b bytes of traffic instead of
- * 6*N*S_b.
+ * 6*N*S_b. For a plan of fp32 gradients in bf16 buckets (ddp_bucket_plan_ex:
+ * DDP's bf16 compression hook on gradients that are the bucket) every
+ * gradient is rounded to bf16 as it enters the sum, each add is rounded to
+ * bf16, and scale * sum is rounded once to fp32: again bit for bit the
+ * copying path, with no bf16 bucket.
  *   grad_arenas[N]: device pointers, 16-byte aligned, each arena_numel elements
  *       laid out by ddp_plan_grad_arena; read and overwritten (members only).
  *   N must equal the plan's world size. */

@@ -92,7 +92,7 @@ extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params,
       pos += round_up(param_numels[p], va);
     }
     plan->arena_numel = pos;
-    if (comm_dtype == grad_dtype) plan->vec_info.assign(pos / va, kVecSlack);
+    plan->vec_info.assign(pos / va, kVecSlack);
 
     // Buckets: reverse registration order.
     Bucket open;
@@ -153,9 +153,13 @@ extern "C" int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params,
       }
 
       for (const Member& m : b.members) b.data_numel += m.numel;
-      // The in-place sync (same dtypes only): the bucket's members are a run
-      // of consecutive parameters, so they span one stretch of the arena.
-      if (comm_dtype == grad_dtype && !b.members.empty()) {
+      // The in-place sync: the bucket's members are a run of consecutive
+      // parameters, so they span one stretch of the arena. Each arena vector
+      // lies in one ring chunk: arena offsets are multiples of va, bucket
+      // offsets and the chunk length L multiples of v, and va <= v (with
+      // bf16 buckets, an fp32 arena vector of 4 elements sits inside one
+      // 8-element bucket vector).
+      if (!b.members.empty()) {
         const Member& last = b.members.back();    // lowest parameter index
         const Member& first = b.members.front();  // highest
         b.view_vec_begin = plan->arena_offsets[last.param] / va;
@@ -215,8 +219,6 @@ extern "C" int ddp_plan_member(const ddp_plan* plan, int32_t b, int32_t i, int32
 
 extern "C" int ddp_plan_arena_map(const ddp_plan* plan, uint16_t* out, int64_t n) {
   if (plan == nullptr || (out == nullptr && n > 0)) return fail(DDP_EINVAL, "ddp_plan_arena_map: NULL argument");
-  if (plan->comm_dtype != plan->dtype)
-    return fail(DDP_EINVAL, "ddp_plan_arena_map: the plan has no in-place map (buckets of another dtype)");
   if (n != int64_t(plan->vec_info.size()))
     return fail(DDP_EINVAL, "ddp_plan_arena_map: n must be the arena's vector count (" +
                                 std::to_string(plan->vec_info.size()) + ")");

@@ -31,11 +31,42 @@
 // ~0.05 ms of a 0.30 ms sync, where one-wave blocks that each read all N
 // ranks exposed ~0.21 ms of it. Stores are non-temporal; loads are too when
 // the ranks' arenas together exceed the Infinity Cache.
+//
+// A plan with fp32 gradients and bf16 buckets (the bf16 compression hook;
+// page "Day 17 数据并行 DP/DDP", reading list, "PyTorch DDP Communication
+// Hooks") syncs in place too, like DDP with gradient_as_bucket_view=True and
+// the bf16 hook: the fp32 gradients are the bucket, and the hook rounds them
+// to bf16, all-reduces in bf16 and writes the result back in fp32. Per
+// element: each rank's gradient is rounded to bf16 as it enters the ring,
+// every hop adds in bf16 with one rounding, and the sum times `scale` is
+// rounded once to fp32: bit for bit the bf16 pack, the bf16 ring and the
+// copy back to fp32, with no bf16 bucket in memory.
 #include <algorithm>
 
 #include "ring_common.h"
 
 namespace ddp {
+
+// Element type of the in-place sync of a compressed plan: fp32 in memory,
+// bf16 in the ring's arithmetic.
+constexpr int kF32ViaBf16 = 2;
+
+template <>
+struct Ops<kF32ViaBf16> : Ops<DDP_FP32> {};
+
+template <>
+struct Word<kF32ViaBf16> {
+  struct Acc {
+    float v;  // a bf16 value, as an fp32 number with the low 16 bits clear
+  };
+  static __device__ __forceinline__ Acc from(uint32_t w) { return Acc{round_bf16(__uint_as_float(w))}; }
+  static __device__ __forceinline__ void add(Acc& a, uint32_t w) {
+    a.v = round_bf16(a.v + round_bf16(__uint_as_float(w)));
+  }
+  static __device__ __forceinline__ uint32_t out(const Acc& a, float s) { return __float_as_uint(a.v * s); }
+  static __device__ __forceinline__ float elem(u32x4 y, int j) { return __uint_as_float(y[j]); }
+};
+
 namespace {
 
 constexpr int kViewMaxWaves = 8;  // waves per block (one rank each, or every 8th rank when N > 8)
@@ -172,6 +203,26 @@ void launch_view(const ViewSpan& sp, const RankPtrs& P, int n, float scale, int6
   }
 }
 
+// The kernels for the plan's dtypes (a compressed plan's arithmetic goes
+// through bf16), with non-temporal loads when the ranks' arenas together
+// exceed the Infinity Cache: buckets are reduced one after the other over
+// the whole arena, so the arena's size, not one bucket's, decides whether
+// loads can hit the cache.
+void launch_view_plan(const ddp_plan* plan, const ViewSpan& sp, const RankPtrs& P, int N, float scale,
+                      int64_t max_blocks, hipStream_t s) {
+  const bool ntl = int64_t(N) * plan->arena_numel * elem_bytes(plan->dtype) > kInfinityCacheBytes;
+  if (plan->dtype != plan->comm_dtype) {
+    if (ntl) launch_view<kF32ViaBf16, true>(sp, P, N, scale, max_blocks, s);
+    else launch_view<kF32ViaBf16, false>(sp, P, N, scale, max_blocks, s);
+  } else if (plan->dtype == DDP_FP32) {
+    if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, max_blocks, s);
+    else launch_view<DDP_FP32, false>(sp, P, N, scale, max_blocks, s);
+  } else {
+    if (ntl) launch_view<DDP_BF16, true>(sp, P, N, scale, max_blocks, s);
+    else launch_view<DDP_BF16, false>(sp, P, N, scale, max_blocks, s);
+  }
+}
+
 }  // namespace
 }  // namespace ddp
 
@@ -186,18 +237,8 @@ int launch_view_bucket(const ddp_plan* plan, int32_t b, const RankPtrs& P, int32
   const uint16_t* info = nullptr;
   int st = device_tables(const_cast<ddp_plan*>(plan), nullptr, &info);
   if (st != DDP_OK) return st;
-  const int eb = elem_bytes(plan->dtype);
-  // Buckets are reduced one after the other over the whole arena, so the
-  // arena's size, not one bucket's, decides whether loads can hit the cache.
-  const bool ntl = int64_t(N) * plan->arena_numel * eb > kInfinityCacheBytes;
   const ViewSpan sp{info, bk.view_vec_begin / kViewThreads, bk.n_view_tiles, bk.view_vec_begin, bk.view_vec_end};
-  if (plan->dtype == DDP_FP32) {
-    if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, max_blocks, s);
-    else launch_view<DDP_FP32, false>(sp, P, N, scale, max_blocks, s);
-  } else {
-    if (ntl) launch_view<DDP_BF16, true>(sp, P, N, scale, max_blocks, s);
-    else launch_view<DDP_BF16, false>(sp, P, N, scale, max_blocks, s);
-  }
+  launch_view_plan(plan, sp, P, N, scale, max_blocks, s);
   DDP_HIP_TRY(hipGetLastError(), "bucket_allreduce_view: launch");
   return DDP_OK;
 }
@@ -208,23 +249,13 @@ int launch_view_arena(const ddp_plan* plan, const RankPtrs& P, int32_t N, float 
   const uint16_t* info = nullptr;
   int st = device_tables(const_cast<ddp_plan*>(plan), nullptr, &info);
   if (st != DDP_OK) return st;
-  const int eb = elem_bytes(plan->dtype);
-  const bool ntl = int64_t(N) * plan->arena_numel * eb > kInfinityCacheBytes;
   const ViewSpan sp{info, 0, (vecs + kViewThreads - 1) / kViewThreads, 0, vecs};
-  if (plan->dtype == DDP_FP32) {
-    if (ntl) launch_view<DDP_FP32, true>(sp, P, N, scale, 0, s);
-    else launch_view<DDP_FP32, false>(sp, P, N, scale, 0, s);
-  } else {
-    if (ntl) launch_view<DDP_BF16, true>(sp, P, N, scale, 0, s);
-    else launch_view<DDP_BF16, false>(sp, P, N, scale, 0, s);
-  }
+  launch_view_plan(plan, sp, P, N, scale, 0, s);
   DDP_HIP_TRY(hipGetLastError(), "ddp_sync: launch");
   return DDP_OK;
 }
 
 int check_view_arenas(const ddp_plan* plan, void* const* grad_arenas, int32_t N, const char* fn) {
-  if (plan->comm_dtype != plan->dtype)
-    return fail(DDP_EINVAL, std::string(fn) + ": the in-place sync needs buckets of the gradients' dtype");
   const int eb = elem_bytes(plan->dtype);
   return check_rank_buffers(grad_arenas, N, plan->arena_numel * eb, 16, fn, "grad_arenas");
 }

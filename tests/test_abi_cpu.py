@@ -188,7 +188,8 @@ def test_compressed_plan_errors():
                   rar.DDP_EINVAL, "mixed pair")
     p = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
     bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
-    expect_status(lib.bucket_allreduce_view(p.handle, 0, bufs, 2, 0.5, None), rar.DDP_EINVAL, "gradients' dtype")
+    # the in-place sync accepts the compressed plan and checks its fp32 arenas
+    expect_status(lib.bucket_allreduce_view(p.handle, 0, bufs, 2, 0.5, None), rar.DDP_EINVAL, "device allocation")
 
 
 def test_reducer_argument_errors():
@@ -209,13 +210,14 @@ def test_reducer_argument_errors():
     expect_status(lib.ddp_synthetic_backward(bufs, bufs, 2, 10, rar.DDP_FP32, 1, 65, None), rar.DDP_EINVAL, "lds_kib")
 
 
-def expected_arena_map(numels, elem_bytes, cap, first, n):
+def expected_arena_map(numels, elem_bytes, cap, first, n, bucket_vector_elems=None):
     """The in-place sync's per-vector map, derived from the oracle's plan and
-    an arena laid out in registration order on V-element boundaries."""
+    an arena laid out in registration order on V-element boundaries.
+    bucket_vector_elems = 8 with fp32 gradients: the plan of bf16 buckets."""
     v = 16 // elem_bytes
     offs = np.concatenate([[0], np.cumsum([-(-m // v) * v for m in numels])]).astype(np.int64)
     out = np.full(int(offs[-1]) // v, 0xFFFF, dtype=np.uint16)
-    for b in planner.plan(numels, elem_bytes, cap, first, n):
+    for b in planner.plan(numels, elem_bytes, cap, first, n, vector_elems=bucket_vector_elems):
         L = b["padded_numel"] // n
         for p, off, m in b["members"]:
             for e in range(0, m, v):
@@ -238,6 +240,20 @@ def test_arena_map_matches_oracle_plan(seed):
     assert np.array_equal(p.arena_map(), expected_arena_map(numels, eb, cap, first, n))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_compressed_arena_map_matches_oracle_plan(seed):
+    """fp32 gradients in bf16 buckets: one map entry per 4-element fp32 arena
+    vector, its chunk taken from the bf16 buckets' layout (8-element vectors),
+    so no arena vector straddles a chunk boundary."""
+    rng = np.random.default_rng(3000 + seed)
+    numels = [int(x) for x in rng.integers(0, 3000, size=rng.integers(1, 40))]
+    cap = int(rng.integers(64, 20000))
+    first = int(rng.integers(64, 20000))
+    n = [1, 2, 3, 8, 13, 64][seed]
+    p = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", cap, first, n)
+    assert np.array_equal(p.arena_map(), expected_arena_map(numels, 4, cap, first, n, bucket_vector_elems=8))
+
+
 def test_arena_map_resnet50():
     numels = resnet50_param_numels()
     p = rar.ddp_bucket_plan(numels, "fp32", world_size=8)
@@ -253,4 +269,5 @@ def test_arena_map_errors():
     assert lib.ddp_plan_arena_map(p.handle, out, 3) == rar.DDP_OK   # 4 + 8 fp32 elements: 3 vectors
     expect_status(lib.ddp_plan_arena_map(p.handle, out, 2), rar.DDP_EINVAL, "vector count")
     pc = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
-    expect_status(lib.ddp_plan_arena_map(pc.handle, out, 3), rar.DDP_EINVAL, "another dtype")
+    assert lib.ddp_plan_arena_map(pc.handle, out, 3) == rar.DDP_OK   # the compressed plan's fp32 arena
+    expect_status(lib.ddp_plan_arena_map(pc.handle, out, 4), rar.DDP_EINVAL, "vector count")

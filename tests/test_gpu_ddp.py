@@ -177,17 +177,18 @@ def test_resnet50_sync(resnet50_case, variant):
             assert_bit_equal(got[r][p], want[r][p], f"{variant} rank {r} param {p}")
 
 
-@pytest.mark.parametrize("variant", ["fused", "steps", "persistent"])
-@pytest.mark.parametrize("n", [2, 3, 8, 16])
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 13, 16, 64])
 def test_bf16_compressed_sync(variant, n):
-    """fp32 gradients synced through bf16 buckets (the bf16 compression hook)
-    equal the oracle's compressed sync bit for bit."""
+    """fp32 gradients synced through bf16 buckets (the bf16 compression hook),
+    or through bf16 arithmetic on the gradients in place (view), equal the
+    oracle's compressed sync bit for bit."""
     numels = [1, 3000, 17, 0, 65, 40000, 2, 129, 7777, 5]
     cap, first = 64 * 1024, 512
     plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", cap, first, n)
     grads = host_grads(60 + n, n, numels)
     arenas, offs = make_arenas(plan, grads, "fp32")
-    buckets = bucket_buffers(plan, n, "bf16")
+    buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
     rar.ddp_sync(plan, arenas, buckets, variant=variant)
     torch.cuda.synchronize()
     if variant == "persistent":
@@ -200,14 +201,15 @@ def test_bf16_compressed_sync(variant, n):
             assert_bit_equal(got[r][p], want[r][p], f"{variant} n={n} rank {r} param {p}")
 
 
-def test_bf16_compressed_resnet50():
+@pytest.mark.parametrize("variant", ["fused", "view"])
+def test_bf16_compressed_resnet50(variant):
     w = WORKLOADS["ddp_resnet50"]
     numels = resnet50_param_numels()
     grads = host_grads(w.seed, w.n, numels, std=w.std)
     plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=w.n)
     arenas, offs = make_arenas(plan, grads, "fp32")
-    buckets = bucket_buffers(plan, w.n, "bf16")
-    rar.ddp_sync(plan, arenas, buckets, variant="fused", scale=0.125)
+    buckets = None if variant == "view" else bucket_buffers(plan, w.n, "bf16")
+    rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=0.125)
     torch.cuda.synchronize()
     got = read_grads(arenas, offs, numels, "fp32")
     want = ddp.ddp_sync(grads, planner.plan(numels, 4, world_size=w.n, vector_elems=8), "fp32",
@@ -217,11 +219,27 @@ def test_bf16_compressed_resnet50():
             assert_bit_equal(got[r][p], want[r][p], f"rank {r} param {p}")
 
 
-def test_view_refuses_compressed_plan():
-    plan = rar.ddp_bucket_plan_ex([100, 200], "fp32", "bf16", world_size=2)
-    arenas, _ = make_arenas(plan, host_grads(1, 2, [100, 200]), "fp32")
-    with pytest.raises(rar.DDPError, match="gradients' dtype"):
-        rar.ddp_sync(plan, arenas, None, variant="view")
+@pytest.mark.parametrize("n", [3, 8])
+def test_view_compressed_special_values(n):
+    """The in-place compressed sync on values whose bf16 rounding matters:
+    halfway cases, values that overflow bf16, subnormals and signed zeros,
+    against the oracle's compressed sync."""
+    rng = np.random.default_rng(90 + n)
+    # One sign of the near-maximal value only: sums may overflow to +inf, never meet -inf (inf - inf would
+    # give a NaN whose bits differ between processors).
+    special = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, -(1.0 + 2.0 ** -8), 3.3895e38,
+                        1e-40, -1e-40, 2.0 ** -133, 0.0, -0.0, 65504.0, 1.0 - 2.0 ** -9], dtype=np.float32)
+    numels = [37, 1000, 5]
+    plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", 4096, 256, n)
+    grads = [[rng.choice(special, size=m).astype(np.float32) for m in numels] for _ in range(n)]
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    rar.ddp_sync(plan, arenas, None, variant="view")
+    torch.cuda.synchronize()
+    got = read_grads(arenas, offs, numels, "fp32")
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, 4096, 256, n, vector_elems=8), "fp32", comm_dtype="bf16")
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"rank {r} param {p}")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

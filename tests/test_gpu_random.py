@@ -109,7 +109,7 @@ def draw_sync_cases(seed=20261203):
     """Random parameter lists (1 to 40 tensors, sizes log-uniform up to 200k,
     some empty or single-element), bucket capacities from 4 KiB to 25 MiB,
     1 to 13 ranks, fp32 or bf16 gradients or the bf16 compression hook, and
-    every sync variant (in place only for same-dtype plans)."""
+    every sync variant."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(N_SYNC_CASES):
@@ -119,8 +119,7 @@ def draw_sync_cases(seed=20261203):
         first = int(rng.choice([256, 4096, 1 << 20]))
         n = int(rng.choice([1, 2, 3, 4, 5, 8, 8, 13]))
         kind = str(rng.choice(["fp32", "bf16", "fp32_to_bf16"]))
-        variants = ["fused", "steps", "persistent"] + ([] if kind == "fp32_to_bf16" else ["view"])
-        variant = str(rng.choice(variants))
+        variant = str(rng.choice(["fused", "steps", "persistent", "view"]))
         cases.append((i, numels, cap, first, n, kind, variant))
     return cases
 

@@ -56,6 +56,26 @@ def test_reducer_matches_oracle(variant, order):
     check(arenas, offs, NUMELS, want, n, f"{variant}/{order}")
 
 
+@pytest.mark.parametrize("variant,blocks", [("view", 0), ("view", 3), ("fused", 0)])
+def test_reducer_compressed_plan(variant, blocks):
+    """fp32 gradients through bf16 (the compression hook), bucket by bucket as
+    they become ready: in place on the gradients or through bf16 buckets, with
+    and without a cap on the in-place launches' width."""
+    n, cap, first = 5, 64 * 1024, 512
+    plan = rar.ddp_bucket_plan_ex(NUMELS, "fp32", "bf16", cap, first, n)
+    grads = host_grads(71, n, NUMELS)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
+    want = ddp.ddp_sync(grads, planner.plan(NUMELS, 4, cap, first, n, vector_elems=8), "fp32", comm_dtype="bf16")
+    comm = torch.cuda.Stream()
+    red = rar.Reducer(plan, arenas, buckets, variant=variant, comm_stream=comm, comm_max_blocks=blocks)
+    for p in reversed(range(len(NUMELS))):
+        red.mark_ready(p)
+    red.finalize()
+    torch.cuda.synchronize()
+    check(arenas, offs, NUMELS, want, n, f"compressed {variant}")
+
+
 def test_reducer_reports_a_missing_gradient_and_recovers():
     n = 2
     plan, grads, arenas, offs, buckets, want = setup("view", n)
