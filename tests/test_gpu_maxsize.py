@@ -1,8 +1,11 @@
-"""GPU parity where one chunk (fused all-reduce) or one arena (in-place sync)
-has more tiles than one launch's grid holds (2^22 tiles), so the launcher
-splits the work over several launches. Two ranks, fp32, 8.6 GB and 4.3 GB
-per rank; sampled positions, including both sides of every split, against
-the oracle. Memory: ~17 GB of HBM for the first test, ~9 GB for the second."""
+"""GPU parity where one chunk (fused all-reduce, reduce-scatter output) or
+one arena (in-place sync) has more tiles than one launch's grid holds (2^22
+tiles), so the launcher splits the work over several launches (or, for the
+reduce-scatter output, the blocks loop over the tiles beyond). Two ranks,
+fp32, 8.6 GB and 4.3 GB per rank; sampled positions, including both sides of
+every split, against the oracle. Memory: ~17 GB of HBM for the all-reduce,
+~26 GB for the reduce-scatter (inputs and shards), ~9 GB for the in-place
+sync."""
 
 import numpy as np
 import pytest
@@ -45,6 +48,35 @@ def test_fused_all_reduce_split_over_launches(extra):
     want = ring.ring_simulate(before, "fp32", chunk_of=pos // L)["bufs"]
     for r in range(n):
         assert_bit_equal(after[r], want[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("extra", [4096, 4092])
+def test_reduce_scatter_split_over_launches(extra):
+    """The reduce-scatter output where one chunk has more tiles than one grid
+    holds (the blocks loop over the rest), ending in a whole tile (extra =
+    4096) or a partial one (4092): sampled shard positions, scale 1, equal the
+    ring's sum at those positions."""
+    n = 2
+    L = MAX_GRID_TILES * TILE_FP32 + extra
+    count = n * L
+    bufs = device_ring_inputs(33, n, count, "fp32", std=1e-3)
+    pos = with_edges(sample_positions(count, n, 20000, seed=33), count,
+                     [c * L + MAX_GRID_TILES * TILE_FP32 for c in range(n)])
+    pos_dev = torch.from_numpy(pos).cuda()
+    before = [gather(t, pos_dev, "fp32") for t in bufs]
+    shards = [torch.empty(L, device="cuda") for _ in range(n)]
+    print(f"[reduce-scatter split] N={n} count={count} samples={len(pos)}", flush=True)
+    rar.ring_reduce_scatter_fused(bufs, shards, 1.0)
+    torch.cuda.synchronize()
+    want = ring.ring_simulate(before, "fp32", chunk_of=pos // L)["bufs"][0]
+    chunk = pos // L
+    got = np.empty(len(pos), np.float32)
+    for c in range(n):
+        sel = np.nonzero(chunk == c)[0]
+        got[sel] = gather(shards[c], torch.from_numpy(pos[sel] - c * L).cuda(), "fp32")
+    assert_bit_equal(got, want, "shards")
+    del bufs, shards
+    torch.cuda.empty_cache()
 
 
 def test_in_place_sync_split_over_launches():
