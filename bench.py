@@ -119,6 +119,42 @@ def main():
     from ddp_workloads import WORKLOADS, device_ring_inputs, host_ring_inputs, resnet50_param_numels
 
     torch.cuda.set_device(0)
+    extras = {}
+
+    # ------------------------------------------------------------ 64 ranks x 300M fp32
+    # Measured first, on two sets of buffers: the first 76.8 GB this process
+    # allocates, and a second set allocated while the first is still held.
+    # The same kernel on the same values ran ~20 % slower on the first set
+    # (and on buffers later allocated at its addresses); the step kernels,
+    # which touch two ranks per block, ran alike on both.
+    print("bench: 64 ranks x 300M fp32", file=sys.stderr, flush=True)
+    w5 = WORKLOADS["ring_n64_300m"]
+    S5 = w5.count * 4
+
+    def n64_inputs():
+        return device_ring_inputs(w5.seed, w5.n, w5.count, "fp32", std=w5.std, heavy_frac=w5.heavy_frac,
+                                  heavy_mult=w5.heavy_mult)
+
+    def n64_time(fn, nbytes, launches):
+        fn()
+        t = time_launches(fn, 2, torch)
+        return {"ms": round(t, 3), "bus_gbps": round(gbps(2 * (w5.n - 1) / w5.n * S5, t), 1),
+                "hbm_gbps": round(gbps(nbytes, t), 1), "launches": launches}
+
+    first = n64_inputs()
+    n64_first = n64_time(lambda: rar.ring_allreduce_fused(first), 2 * w5.n * S5, 1)
+    b5 = n64_inputs()
+    n64 = {}
+    for name, fn, nbytes, launches in [
+            ("fused", lambda: rar.ring_allreduce_fused(b5), 2 * w5.n * S5, 1),
+            ("steps", lambda: rar.ring_allreduce_stepwise(b5), 5 * (w5.n - 1) * S5, 2 * (w5.n - 1)),
+            ("persistent", lambda: rar.ring_allreduce_persistent(b5), 5 * (w5.n - 1) * S5, 1)]:
+        n64[name] = n64_time(fn, nbytes, launches)
+    n64["fused_on_first_allocation"] = n64_first
+    rar.ddp_persistent_status()
+    extras["ring_n64_300m"] = n64
+    del b5, first
+    torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ headline: fused, N=8, 1 GiB fp32
     w = WORKLOADS["ring_n8_1gib"]
@@ -146,7 +182,6 @@ def main():
     traffic = traffic_from_profile()
 
     # ------------------------------------------------------------ same workload, other forms
-    extras = {}
     reps = max(3, args.steps // 4)
 
     def stepwise():
@@ -364,25 +399,6 @@ def main():
         overlap["caps"][model]["backward_model"] = {"fma_per_element": work, "reserved_lds_kib_per_block": lds_kib}
     extras["overlap_resnet50_n8"] = overlap
     del arenas, srcs
-    torch.cuda.empty_cache()
-
-    # ------------------------------------------------------------ 64 ranks x 300M fp32
-    w5 = WORKLOADS["ring_n64_300m"]
-    b5 = device_ring_inputs(w5.seed, w5.n, w5.count, "fp32", std=w5.std, heavy_frac=w5.heavy_frac,
-                            heavy_mult=w5.heavy_mult)
-    S5 = w5.count * 4
-    n64 = {}
-    for name, fn, nbytes, launches in [
-            ("fused", lambda: rar.ring_allreduce_fused(b5), 2 * w5.n * S5, 1),
-            ("steps", lambda: rar.ring_allreduce_stepwise(b5), 5 * (w5.n - 1) * S5, 2 * (w5.n - 1)),
-            ("persistent", lambda: rar.ring_allreduce_persistent(b5), 5 * (w5.n - 1) * S5, 1)]:
-        fn()
-        t = time_launches(fn, 2, torch)
-        n64[name] = {"ms": round(t, 3), "bus_gbps": round(gbps(2 * (w5.n - 1) / w5.n * S5, t), 1),
-                     "hbm_gbps": round(gbps(nbytes, t), 1), "launches": launches}
-    rar.ddp_persistent_status()
-    extras["ring_n64_300m"] = n64
-    del b5
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle

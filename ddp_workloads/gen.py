@@ -90,10 +90,16 @@ def device_ring_inputs(seed, n, count, dtype="fp32", std=1e-2, heavy_frac=0.0,
     """N rank buffers drawn on the GPU with torch's generator seeded
     1000 * seed + rank; returns a list of torch tensors (float32 or bfloat16).
 
-    The buffers are generated one at a time to bound the temporaries.
+    All N buffers are allocated before any is drawn, as a trainer allocates
+    its gradient buffers once, so no drawing temporary sits between two of
+    them; the draws then go one rank at a time to bound the temporaries.
+    (With the temporaries interleaved between the buffers, the 64-rank x 300M
+    fused all-reduce ran ~20 % slower on MI355X, although every buffer still
+    began on a 2 MiB boundary.)
     """
     import torch
-    out = []
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = [torch.empty(count, dtype=tdt, device=device) for _ in range(n)]
     for r in range(n):
         g = torch.Generator(device=device)
         g.manual_seed(1000 * seed + r)
@@ -103,7 +109,6 @@ def device_ring_inputs(seed, n, count, dtype="fp32", std=1e-2, heavy_frac=0.0,
             mask = torch.rand(count, generator=g, device=device) < heavy_frac
             x[mask] *= heavy_mult
             del mask
-        if dtype == "bf16":
-            x = x.to(torch.bfloat16)
-        out.append(x)
+        out[r].copy_(x)  # bf16: rounded to nearest even, as .to(torch.bfloat16)
+        del x
     return out

@@ -82,11 +82,16 @@ def test_c1_fused_and_exact_sum():
 # (8, 25), (6, 6141), (8, 7 * 4096 + 4093) and (9, 100_003) end in a partial
 # vector (and (8, 25) in an empty chunk) on the vector path. Equal chunks of
 # whole tiles (64 vectors) take the whole-tile kernel: (2, 4096), (8, 65536),
-# (64, 65536), (7, 10752) and (13, 13312) in both dtypes, (3, 3840) in fp32.
+# (7, 10752) and (13, 13312) in both dtypes, (3, 3840) in fp32. From 60 ranks
+# on, equal chunks of whole vectors take the span kernel instead: (64, 65536)
+# (whole spans), (64, 64000) (chunks that start mid-tile, so spans at both
+# ends are clamped), (61, 61 * 8800) (interior and edge spans), (60, 60 * 8)
+# (one vector per chunk in fp32) and (63, 63 * 2056).
 SHAPES = [(2, 4096), (3, 6), (3, 7), (4, 3), (5, 12345), (6, 6141), (7, 7 * 2048 * 3 + 11),
           (8, 8 * 4096 * 2), (8, 8 * 4096 * 2 + 5), (8, 5), (8, 25), (8, 7 * 4096 + 4093), (9, 100_003),
           (12, 12 * 3001 + 5), (16, 16 * 1000), (33, 33 * 257 + 1), (64, 64 * 1024),
-          (3, 3 * 1280), (7, 7 * 1536), (13, 13 * 1024)]
+          (3, 3 * 1280), (7, 7 * 1536), (13, 13 * 1024),
+          (64, 64 * 1000), (61, 61 * 8800), (60, 60 * 8), (63, 63 * 2056)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
