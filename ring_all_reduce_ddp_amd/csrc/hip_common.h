@@ -45,7 +45,7 @@ int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, c
 bool all_aligned16(void* const* bufs, int32_t n);
 
 // Per-device persistent-barrier words (defined in runtime.hip): *slot receives
-// a device pointer to kSlotWords 32-bit words reserved for one launch, zeroed
+// a device pointer to 64 32-bit words reserved for one launch, zeroed
 // on `stream` ahead of it; *status the device's sticky timeout word.
 int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status);
 

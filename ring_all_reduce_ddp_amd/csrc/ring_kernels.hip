@@ -34,17 +34,20 @@ namespace {
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
 constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
 // Persistent grid, measured on MI355X (14 steps, 8 ranks): 1024-thread blocks.
-// Buffers beyond the Infinity Cache (8 x 1 GiB fp32): three blocks for every
-// four compute units (192): 6.52 ms; 160 to 256 blocks took 6.65, 6.54, 6.52,
-// 6.77, 6.96, 7.08 and 7.23 ms; 256 blocks of 512 threads 6.65 ms; 512 blocks
-// of 256 threads 6.96 ms. Buffers inside it (cached accesses): three blocks
+// Buffers beyond the Infinity Cache (8 x 1 GiB fp32), tiles handed out by
+// tickets: seven blocks for every eight compute units (224): 5.91-5.94 ms;
+// 128, 160, 192 and 256 blocks took 7.63, 6.78, 6.15 and 5.97 ms (64 ranks x
+// 300M: 61.5 ms at 192, 59.8 at 256). With a fixed grid-stride share per
+// block instead, 192 blocks were best at 6.52 ms (160 to 256: 6.65, 6.54,
+// 6.52, 6.77, 6.96, 7.08, 7.23 ms): a step ended when its slowest block did.
+// Buffers inside it (cached accesses): three blocks
 // for every eight compute units (96): 8 x 25 MiB 0.287 ms against 0.344 ms
 // with 192 (16, 32, 64, 128 blocks: 0.756, 0.430, 0.304, 0.295 ms); 8 x 16
 // MiB 0.217 against 0.271 ms. More blocks add barrier arrivals, polling and,
 // with cached stores, write-backs of dirty cache lines at every barrier;
 // fewer leave bandwidth unused.
 constexpr int kPersistentThreads = 1024;   // threads per persistent block
-constexpr int kPersistentBlocksPer8CUsStreaming = 6;
+constexpr int kPersistentBlocksPer8CUsStreaming = 7;
 constexpr int kPersistentBlocksPer8CUsCached = 3;
 
 // ---------------------------------------------------------------- one step
@@ -139,6 +142,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(RankPtrs P, int n, int64_
 // ---------------------------------------------------------------- persistent
 
 constexpr unsigned kAbortBit = 0x80000000u;
+// Word of a launch's barrier slot (64 words, zeroed before the launch) that
+// holds the tile-ticket counter: its own 128-byte line, away from the
+// arrival counter in word 0 that waiting blocks poll.
+constexpr int kTicketWord = 32;
 
 // Grid-wide barrier for a cooperative launch. counter[0] counts arrivals over
 // the whole launch; its top bit is the launch's abort flag. A block that has
@@ -185,13 +192,51 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
                                                          unsigned int* counter, unsigned int* status,
                                                          unsigned long long deadline, unsigned int extra) {
   const int64_t total_tiles = int64_t(n) * tiles_per_chunk;
-  for (int i = 0; i < n_steps; ++i) {
-    const int phase = i < n - 1 ? DDP_RS : DDP_AG;
-    const int s = i < n - 1 ? i : i - (n - 1);
-    for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
-      step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
-    if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
-      return;
+  if constexpr (NT) {
+    // Tiles handed out by one ticket counter for the whole launch: tickets
+    // [i * total, (i + 1) * total) are step i's tiles. A block takes its next
+    // ticket while it works on the current tile; the one ticket past its
+    // step that every block ends a step holding is a tile of the next step,
+    // since the grid never exceeds one step's tiles. Thread 0 draws, and a
+    // double-buffered LDS word passes the ticket to the block with one
+    // barrier per tile.
+    unsigned int* tickets = counter + kTicketWord;
+    __shared__ unsigned int next_ticket[2];
+    if (threadIdx.x == 0)
+      next_ticket[0] = __hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    unsigned int t = next_ticket[0];
+    int k = 1;
+    for (int i = 0; i < n_steps; ++i) {
+      const int phase = i < n - 1 ? DDP_RS : DDP_AG;
+      const int s = i < n - 1 ? i : i - (n - 1);
+      const unsigned int end = unsigned(i + 1) * unsigned(total_tiles);
+      while (t < end) {
+        unsigned int drawn = 0u;
+        if (threadIdx.x == 0)
+          drawn = __hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk,
+                                                                int64_t(t) - int64_t(i) * total_tiles, s, phase);
+        if (threadIdx.x == 0) next_ticket[k & 1] = drawn;
+        __syncthreads();
+        t = next_ticket[k & 1];
+        ++k;
+      }
+      if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
+        return;
+    }
+  } else {
+    // Buffers inside the Infinity Cache: a fixed grid-stride share per block
+    // (tickets measured 1-2 % slower here: 8 x 25 MiB 0.299-0.301 against
+    // 0.295-0.297 ms at 96 blocks).
+    for (int i = 0; i < n_steps; ++i) {
+      const int phase = i < n - 1 ? DDP_RS : DDP_AG;
+      const int s = i < n - 1 ? i : i - (n - 1);
+      for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
+        step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
+      if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
+        return;
+    }
   }
 }
 
@@ -268,6 +313,9 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
   unsigned grid = 0;
   int st = persistent_grid<DT, VEC, NT>(a, o.max_blocks, &grid, &cus);
   if (st != DDP_OK) return st;
+  // Tickets are 32-bit: every tile of every step, plus one per block.
+  if (int64_t(n_steps) * tpc * a.n + grid >= (int64_t(1) << 32))
+    return fail(DDP_EINVAL, "ring_allreduce_persistent: too many tiles for one launch");
   DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent: hipGetDevice");
   DDP_HIP_TRY(hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev),
               "ring_allreduce_persistent: wall clock rate");
