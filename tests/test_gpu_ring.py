@@ -260,3 +260,45 @@ def test_persistent_grid_sizes(max_blocks):
     rar.ddp_persistent_status()
     for r in range(8):
         assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"max_blocks={max_blocks} rank {r}")
+
+
+# Buffers beyond the 256 MiB Infinity Cache take the persistent kernel whose
+# tiles are handed out by a ticket counter: 8 ranks x (8 x 1,100,000 + 3)
+# fp32 (282 MB; chunk lengths that are not whole vectors, a short last chunk).
+BIG_N, BIG_COUNT = 8, 8 * 1_100_000 + 3
+
+
+@pytest.fixture(scope="module")
+def big_inputs():
+    return host_ring_inputs(34, BIG_N, BIG_COUNT, "fp32")
+
+
+@pytest.mark.parametrize("n_steps,max_blocks", [(1, 0), (8, 0), (14, 0), (14, 17), (14, 1000), (13, 61)])
+def test_persistent_tickets_beyond_cache(big_inputs, n_steps, max_blocks):
+    """Partial and full step counts and several grids on the ticketed path
+    give the oracle's state after that many steps, bit for bit."""
+    assert BIG_N * BIG_COUNT * 4 > 256 << 20
+    want = ring.ring_simulate(big_inputs, "fp32", n_steps=n_steps)["bufs"]
+    dev = to_device(big_inputs, "fp32")
+    rar.ring_allreduce_persistent_ex(dev, n_steps=n_steps, max_blocks=max_blocks)
+    torch.cuda.synchronize()
+    rar.ddp_persistent_status()
+    for r in range(BIG_N):
+        assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"steps={n_steps} max_blocks={max_blocks} rank {r}")
+
+
+def test_persistent_tickets_timeout_path(big_inputs):
+    """The time-out path on the ticketed kernel: every block leaves at the
+    barrier it cannot pass, the status call reports it once, and a normal
+    launch afterwards is exact."""
+    dev = to_device(big_inputs, "fp32")
+    rar.ring_allreduce_persistent_ex(dev, extra_arrivals=1, timeout_us=20_000)
+    torch.cuda.synchronize()
+    with pytest.raises(rar.DDPError, match="timed out"):
+        rar.ddp_persistent_status()
+    rar.ddp_persistent_status()
+    dev = to_device(big_inputs, "fp32")
+    run_variant("persistent", dev)
+    want = ring.ring_simulate(big_inputs, "fp32")["bufs"]
+    for r in range(BIG_N):
+        assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"after a time-out, rank {r}")
