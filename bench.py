@@ -124,9 +124,9 @@ def main():
     # ------------------------------------------------------------ 64 ranks x 300M fp32
     # Measured first, on two sets of buffers: the first 76.8 GB this process
     # allocates, and a second set allocated while the first is still held.
-    # The same kernel on the same values ran ~20 % slower on the first set
-    # (and on buffers later allocated at its addresses); the step kernels,
-    # which touch two ranks per block, ran alike on both.
+    # The same kernel on the same values usually ran ~20 % slower on the
+    # first set (and on buffers later allocated at its addresses); the step
+    # kernels, which touch two ranks per block, ran alike on both.
     print("bench: 64 ranks x 300M fp32", file=sys.stderr, flush=True)
     w5 = WORKLOADS["ring_n64_300m"]
     S5 = w5.count * 4
@@ -150,6 +150,11 @@ def main():
             ("steps", lambda: rar.ring_allreduce_stepwise(b5), 5 * (w5.n - 1) * S5, 2 * (w5.n - 1)),
             ("persistent", lambda: rar.ring_allreduce_persistent(b5), 5 * (w5.n - 1) * S5, 1)]:
         n64[name] = n64_time(fn, nbytes, launches)
+    # reduce-scatter output: every rank's 1/N shard of the sum (reads N*S, writes S)
+    shards5 = [torch.empty(w5.count // w5.n, device="cuda") for _ in range(w5.n)]
+    n64["reduce_scatter_fused"] = n64_time(lambda: rar.ring_reduce_scatter_fused(b5, shards5, 1.0 / w5.n),
+                                           (w5.n + 1) * S5, 1)
+    del shards5
     n64["fused_on_first_allocation"] = n64_first
     rar.ddp_persistent_status()
     extras["ring_n64_300m"] = n64

@@ -244,58 +244,14 @@ __global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_any(Ra
 }
 
 // ---------------------------------------------------------------- many ranks
-//
-// With many ranks (kSpanMinRanks and up) a block that stages one tile of
-// every rank touches N rank buffers, N distinct pages, at once, and the
-// per-CU address-translation cache misses on ~5 % of requests at 64 ranks
-// (0.01 % at 8). Here a block instead walks one span of kSpanVecs x
-// kSpanThreads vectors of its chunk rank by rank, in the chunk's ring order,
-// keeping the running sums in registers, and then writes the span to every
-// rank: at any moment it reads one rank's pages. Same adds in the same
-// order, so the same bits. Measured on MI355X at 64 ranks: 300M fp32
-// 24.8 ms (6.2 TB/s) against 27.4 ms staged, 2^28 fp32 22.3 against 25.0 ms,
-// 2^28 bf16 11.1 against 13.0 ms. At 24, 32 and 40 ranks the two forms ran
-// alike, and at 52 and 56 the staged one was as fast or 1.5 % faster, so
-// the span form starts between 56 and 64. Equal chunks of whole vectors only
-// (count = N * L, L a multiple of V). Spans lie on a grid that starts at the
-// chunk's start rounded down to 64 vectors (1 KiB), so interior spans begin
-// on cache-line boundaries; the spans at a chunk's two ends clamp their
-// loads into the chunk and store only their own vectors.
-
-constexpr int kSpanThreads = 256;
-constexpr int kSpanVecs = 4;       // vectors per thread per rank
-constexpr int kSpanMinRanks = 60;
+// The span form of the fused all-reduce (spans: ring_common.h): each block
+// sums one span of its chunk rank by rank and then writes it to every rank.
 
 template <int DT, bool NTL, bool EDGE>
-__device__ __forceinline__ void span_ring_sum(const RankPtrs& P, int n, int c, int64_t lo, int64_t hi,
-                                              int64_t v0) {
+__device__ __forceinline__ void span_allreduce(const RankPtrs& P, int n, int c, int64_t lo, int64_t hi, int64_t v0) {
   using O = Ops<DT>;
-  int64_t at[kSpanVecs];
-#pragma unroll
-  for (int j = 0; j < kSpanVecs; ++j) {
-    const int64_t v = v0 + int64_t(j) * kSpanThreads;
-    at[j] = EDGE ? std::min(std::max(v, lo), hi - 1) : v;
-  }
-  // Ring order of chunk c: rank c+1 first, then c+2, ..., c.
-  int r = wrap(c + 1, n);
   typename O::Acc acc[kSpanVecs];
-  {
-    const u32x4* src = static_cast<const u32x4*>(P.p[r]);
-    u32x4 x[kSpanVecs];
-#pragma unroll
-    for (int j = 0; j < kSpanVecs; ++j) x[j] = ld16<NTL>(src + at[j]);
-#pragma unroll
-    for (int j = 0; j < kSpanVecs; ++j) acc[j] = O::from(x[j]);
-  }
-  for (int k = 1; k < n; ++k) {
-    r = r + 1 == n ? 0 : r + 1;
-    const u32x4* src = static_cast<const u32x4*>(P.p[r]);
-    u32x4 x[kSpanVecs];
-#pragma unroll
-    for (int j = 0; j < kSpanVecs; ++j) x[j] = ld16<NTL>(src + at[j]);
-#pragma unroll
-    for (int j = 0; j < kSpanVecs; ++j) O::add(acc[j], x[j]);
-  }
+  span_ring_sum<DT, NTL, EDGE>(P, n, c, lo, hi, v0, acc);
   u32x4 y[kSpanVecs];
 #pragma unroll
   for (int j = 0; j < kSpanVecs; ++j) y[j] = O::to(acc[j]);
@@ -313,16 +269,15 @@ __device__ __forceinline__ void span_ring_sum(const RankPtrs& P, int n, int c, i
 // in vectors.
 template <int DT, bool NTL>
 __global__ __launch_bounds__(kSpanThreads) void k_fused_span(RankPtrs P, int n, int64_t Lv, int64_t s0) {
-  constexpr int64_t kSpan = int64_t(kSpanVecs) * kSpanThreads;
   const int c = int(blockIdx.y);
   const int64_t lo = int64_t(c) * Lv;
   const int64_t hi = lo + Lv;
-  const int64_t b0 = lo / kFusedThreads * kFusedThreads + (s0 + int64_t(blockIdx.x)) * kSpan;
+  const int64_t b0 = span_start(lo, s0 + int64_t(blockIdx.x));
   if (b0 >= hi) return;
-  if (b0 >= lo && b0 + kSpan <= hi)
-    span_ring_sum<DT, NTL, false>(P, n, c, lo, hi, b0 + threadIdx.x);
+  if (b0 >= lo && b0 + kSpanLen <= hi)
+    span_allreduce<DT, NTL, false>(P, n, c, lo, hi, b0 + threadIdx.x);
   else
-    span_ring_sum<DT, NTL, true>(P, n, c, lo, hi, b0 + threadIdx.x);
+    span_allreduce<DT, NTL, true>(P, n, c, lo, hi, b0 + threadIdx.x);
 }
 
 // ---------------------------------------------------------------- one element per thread
@@ -428,10 +383,8 @@ void launch_fused_any(const RingArgs& a, hipStream_t s) {
 
 template <int DT, bool NTL>
 void launch_fused_span(const RingArgs& a, hipStream_t s) {
-  constexpr int64_t kSpan = int64_t(kSpanVecs) * kSpanThreads;
   const int64_t Lv = a.L / Ops<DT>::V;
-  // The span grid of a chunk starts up to 63 vectors before the chunk.
-  const int64_t spc = (Lv + kFusedThreads - 1 + kSpan - 1) / kSpan;
+  const int64_t spc = spans_per_chunk(Lv);
   for (int64_t s0 = 0; s0 < spc; s0 += kMaxGrid) {
     const dim3 g(unsigned(std::min(spc - s0, kMaxGrid)), unsigned(a.n));
     hipLaunchKernelGGL((k_fused_span<DT, NTL>), g, dim3(kSpanThreads), 0, s, a.P, a.n, Lv, s0);

@@ -140,6 +140,46 @@ __global__ __launch_bounds__(kThreads) void k_scatter_scalar(RankPtrs P, RankPtr
   }
 }
 
+// Many ranks, equal chunks of whole vectors (spans: ring_common.h): each
+// block sums one span of its chunk rank by rank, then writes the scaled sums
+// to the chunk's shard. Grid: (spans of a chunk from span s0 on, N chunks).
+template <int DT, bool NTL, bool EDGE>
+__device__ __forceinline__ void span_scatter(const RankPtrs& P, void* shard, int n, int c, int64_t lo, int64_t hi,
+                                             int64_t v0, float scale) {
+  using O = Ops<DT>;
+  typename O::Acc acc[kSpanVecs];
+  span_ring_sum<DT, NTL, EDGE>(P, n, c, lo, hi, v0, acc);
+#pragma unroll
+  for (int j = 0; j < kSpanVecs; ++j) {
+    const int64_t v = v0 + int64_t(j) * kSpanThreads;
+    if (!EDGE || (v >= lo && v < hi)) st16<true>(static_cast<u32x4*>(shard) + (v - lo), O::scale(O::to(acc[j]), scale));
+  }
+}
+
+template <int DT, bool NTL>
+__global__ __launch_bounds__(kSpanThreads) void k_scatter_span(RankPtrs P, RankPtrs S, int n, int64_t Lv, int64_t s0,
+                                                               float scale) {
+  const int c = int(blockIdx.y);
+  const int64_t lo = int64_t(c) * Lv;
+  const int64_t hi = lo + Lv;
+  const int64_t b0 = span_start(lo, s0 + int64_t(blockIdx.x));
+  if (b0 >= hi) return;
+  if (b0 >= lo && b0 + kSpanLen <= hi)
+    span_scatter<DT, NTL, false>(P, S.p[c], n, c, lo, hi, b0 + threadIdx.x, scale);
+  else
+    span_scatter<DT, NTL, true>(P, S.p[c], n, c, lo, hi, b0 + threadIdx.x, scale);
+}
+
+template <int DT, bool NTL>
+void launch_scatter_span(const RingArgs& a, const RankPtrs& S, float scale, hipStream_t s) {
+  const int64_t Lv = a.L / Ops<DT>::V;
+  const int64_t spc = spans_per_chunk(Lv);
+  for (int64_t s0 = 0; s0 < spc; s0 += kMaxGrid) {
+    const dim3 g(unsigned(std::min(spc - s0, kMaxGrid)), unsigned(a.n));
+    hipLaunchKernelGGL((k_scatter_span<DT, NTL>), g, dim3(kSpanThreads), 0, s, a.P, S, a.n, Lv, s0, scale);
+  }
+}
+
 template <int DT, bool NTL>
 void launch_scatter_vec(const RingArgs& a, const RankPtrs& S, float scale, hipStream_t s) {
   constexpr int V = Ops<DT>::V;
@@ -192,7 +232,12 @@ void launch_scatter_any(const RingArgs& a, const RankPtrs& S, float scale, hipSt
 template <int DT>
 int launch_scatter(const RingArgs& a, const RankPtrs& S, bool shards_aligned, float scale, hipStream_t s) {
   const bool ntl = int64_t(a.n) * a.count * elem_bytes(DT) > kInfinityCacheBytes;
-  if (a.vec && shards_aligned) {
+  if (a.vec && shards_aligned && a.count == int64_t(a.n) * a.L && a.n >= kSpanMinRanks) {
+    if (ntl)
+      launch_scatter_span<DT, true>(a, S, scale, s);
+    else
+      launch_scatter_span<DT, false>(a, S, scale, s);
+  } else if (a.vec && shards_aligned) {
     if (ntl)
       launch_scatter_vec<DT, true>(a, S, scale, s);
     else

@@ -1,7 +1,7 @@
 """GPU parity of the reduce-scatter output (every rank's gradient shard)
 against the oracle's ring.reduce_scatter, bit for bit: small and ragged
-inputs at several N and both dtypes, and the 8 x 1 GiB workload on sampled
-positions."""
+inputs at several N and both dtypes, and the 8 x 1 GiB and 64 x 300M
+workloads on sampled positions."""
 
 import numpy as np
 import pytest
@@ -29,7 +29,10 @@ def shard_buffers(count, n, dtype):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("n,count", [(1, 100), (2, 4096), (3, 7), (5, 12345), (8, 8 * 2048 * 3),
                                      (8, 8 * 4096 + 5), (8, 5), (8, 25), (8, 7 * 4096 + 4093), (9, 100_003),
-                                     (16, 16 * 1000 + 8), (64, 64 * 1024)])
+                                     (16, 16 * 1000 + 8), (64, 64 * 1024),
+                                     # 60 ranks and up, equal chunks of whole vectors: the span kernel
+                                     # (chunks that start mid-tile, interior and edge spans, one vector)
+                                     (64, 64 * 1000), (61, 61 * 8800), (60, 60 * 8), (63, 63 * 2056)])
 @pytest.mark.parametrize("mean", [False, True])
 def test_shards_against_oracle(dtype, n, count, mean):
     host = host_ring_inputs(n * 7 + count % 13, n, count, dtype, std=1e-2)
@@ -67,17 +70,22 @@ def test_overlapping_shard_refused():
         rar.ring_reduce_scatter_fused(dev, [dev[0][:32], dev[1][32:]])
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_n8_1gib_sampled(dtype):
+@pytest.mark.parametrize("name,dtype", [("ring_n8_1gib", "fp32"), ("ring_n8_1gib", "bf16"),
+                                        ("ring_n64_300m", "fp32")])
+def test_full_size_sampled(name, dtype):
     """Full size: per chunk, k sampled positions from every rank form a small
     ring whose chunks are the samples of the real chunks; the oracle's shards
-    of that small ring equal the GPU shards at those positions."""
-    w = WORKLOADS["ring_n8_1gib"]
+    of that small ring equal the GPU shards at those positions. 8 x 1 GiB in
+    both dtypes; 64 ranks x 300M fp32 (heavy-tailed values) takes the span
+    kernel."""
+    w = WORKLOADS[name]
     count = w.count * (2 if dtype == "bf16" else 1)
     n = w.n
-    bufs = device_ring_inputs(w.seed, n, count, dtype, std=w.std)
+    bufs = device_ring_inputs(w.seed, n, count, dtype, std=w.std, heavy_frac=w.heavy_frac,
+                              heavy_mult=w.heavy_mult)
+    scale = float(np.float32(1) / np.float32(n))
     L = count // n
-    k = 2048
+    k = 2048 if n <= 8 else 256
     rng = np.random.default_rng(4)
     offs = np.sort(np.concatenate([rng.choice(L, k - 4, replace=False), [0, 1, L - 2, L - 1]]))
     offs = np.unique(offs)
@@ -86,10 +94,10 @@ def test_n8_1gib_sampled(dtype):
     pos_dev = torch.from_numpy(pos).cuda()
     mini = [to_host(t.index_select(0, pos_dev), dtype) for t in bufs]
     shards = shard_buffers(count, n, dtype)
-    print(f"[reduce-scatter 8 x 1 GiB {dtype}] samples per chunk={k}", flush=True)
-    rar.ring_reduce_scatter_fused(bufs, shards, 0.125)
+    print(f"[reduce-scatter {name} {dtype}] samples per chunk={k}", flush=True)
+    rar.ring_reduce_scatter_fused(bufs, shards, scale)
     torch.cuda.synchronize()
-    want = ring.reduce_scatter(mini, dtype, 0.125)
+    want = ring.reduce_scatter(mini, dtype, np.float32(scale))
     offs_dev = torch.from_numpy(offs).cuda()
     for c in range(n):
         got = to_host(shards[c].index_select(0, offs_dev), dtype)
