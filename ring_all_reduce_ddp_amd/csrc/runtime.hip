@@ -69,7 +69,8 @@ bool all_aligned16(void* const* bufs, int32_t n) {
 namespace {
 
 constexpr int kSlots = 64;          // launches that may be in flight at once per device
-constexpr int kSlotStride = 64;     // words between slots (256 bytes)
+constexpr int kSlotStride = 64;     // words between slots (256 bytes); a launch uses word 0 (barrier
+                                    // arrivals) and word 32 (the persistent kernel's tile tickets)
 constexpr int kScratchWords = kSlots * kSlotStride + kSlotStride;  // + status line
 
 struct DeviceScratch {
