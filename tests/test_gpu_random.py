@@ -100,6 +100,33 @@ def test_random_case(case):
         assert_bit_equal(to_host(dev[r], dtype), want[r], f"case {i} rank {r}")
 
 
+# ---------------------------------------------------------------- many ranks, equal chunks
+
+N_SPAN_CASES = 16
+
+
+def draw_span_cases(seed=20261204):
+    """60 to 64 ranks and equal chunks of whole vectors (the span kernels of
+    the fused all-reduce and the reduce-scatter output): chunk lengths drawn
+    as random multiples of the vector length, so chunk starts fall anywhere
+    relative to the 64-vector span grid and spans end anywhere in a chunk."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(N_SPAN_CASES):
+        n = int(rng.integers(60, 65))
+        dtype = "fp32" if rng.random() < 0.6 else "bf16"
+        v = 4 if dtype == "fp32" else 8
+        L = v * int(np.exp(rng.uniform(0, np.log(6000))))
+        variant = str(rng.choice(["fused", "reduce_scatter"]))
+        cases.append((100 + i, n, n * L, dtype, (0,) * n, variant))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_span_cases(), ids=lambda c: f"{c[0]}-n{c[1]}-c{c[2]}-{c[3]}-{c[5]}")
+def test_random_span_case(case):
+    test_random_case(case)
+
+
 # ---------------------------------------------------------------- whole DDP syncs
 
 N_SYNC_CASES = 24
