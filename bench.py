@@ -137,7 +137,7 @@ def main():
 
     def n64_time(fn, nbytes, launches):
         fn()
-        t = time_launches(fn, 2, torch)
+        t = time_launches(fn, 5, torch)
         return {"ms": round(t, 3), "bus_gbps": round(gbps(2 * (w5.n - 1) / w5.n * S5, t), 1),
                 "hbm_gbps": round(gbps(nbytes, t), 1), "launches": launches}
 
@@ -323,10 +323,11 @@ def main():
     sizes = [plan.bucket(b)[0] * 4 for b in range(plan.num_buckets)]
     grad_bytes = sum(numels) * 4
     sync = {"bucket_sizes": sizes, "params": len(numels), "grad_bytes_per_rank": grad_bytes}
+    sync_reps = 50  # a sync takes 0.3-2 ms
     for variant in ("fused", "steps", "persistent", "view"):
         bb = None if variant == "view" else buckets
         rar.ddp_sync(plan, arenas, bb, variant=variant)
-        t = time_launches(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), reps, torch)
+        t = time_launches(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), sync_reps, torch)
         sync[variant] = {"ms": round(t, 4),
                          "bus_gbps": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
         if variant in ("fused", "view"):
@@ -344,7 +345,7 @@ def main():
     breakdown = {}
     for name, fn in parts.items():
         fn()
-        t = time_launches(fn, reps, torch)
+        t = time_launches(fn, sync_reps, torch)
         breakdown[name] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
     sync["fused"]["breakdown"] = breakdown
     # the bf16 compression hook: fp32 gradients through bf16 buckets
@@ -352,12 +353,12 @@ def main():
     cbuckets = [[torch.empty(cplan.bucket(b)[0], dtype=torch.bfloat16, device="cuda") for _ in range(wr.n)]
                 for b in range(cplan.num_buckets)]
     rar.ddp_sync(cplan, arenas, cbuckets, variant="fused")
-    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, cbuckets, variant="fused"), reps, torch)
+    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, cbuckets, variant="fused"), sync_reps, torch)
     sync["bf16_compressed_fused"] = {"ms": round(t, 4),
                                      "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
     # the same hook in place: bf16 arithmetic on the fp32 gradients, no bf16 bucket (reads and writes 2*N*S)
     rar.ddp_sync(cplan, arenas, None, variant="view")
-    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, None, variant="view"), reps, torch)
+    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, None, variant="view"), sync_reps, torch)
     sync["bf16_compressed_view"] = {"ms": round(t, 4),
                                     "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1),
                                     "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
