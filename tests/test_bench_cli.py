@@ -1,0 +1,41 @@
+"""The benchmark's command line on the CPU: more than one GPU is refused
+with a message and exit status 2 before anything touches a GPU, and the
+counter-based traffic figure is reported only for the kernel sources it was
+taken on."""
+
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert proc.stdout == ""
+    assert "--gpus 8" in proc.stderr and "one GPU" in proc.stderr
+
+
+def test_traffic_figure_follows_the_kernel_sources():
+    """bench.py reports the counter-based HBM bytes only while the fused
+    kernel's sources hash to the value the counters were taken on."""
+    import hashlib
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        prof = json.load(f)
+    h = hashlib.sha256()
+    for src in prof["kernel_sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    traffic = bench.traffic_from_profile()
+    if h.hexdigest() == prof["kernel_source_sha256"]:
+        assert traffic == prof["hbm_bytes_per_launch"]
+        # within 0.1 % of the headline's algorithmic bytes (2 * 8 ranks * 1 GiB)
+        assert prof["algorithmic_bytes_per_launch"] == 2 * 8 * (1 << 30)
+        assert abs(traffic / prof["algorithmic_bytes_per_launch"] - 1) < 1e-3
+    else:
+        assert traffic is None
+    assert sorted(os.path.join(ROOT, s) for s in prof["kernel_sources"]) == sorted(bench.KERNEL_SOURCES)
