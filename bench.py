@@ -109,7 +109,7 @@ def traffic_from_profile():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs its N virtual ranks on one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the N ranks are virtual and share one GPU; --gpus {args.gpus} is not "
               "supported (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     ensure_library()
