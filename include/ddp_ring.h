@@ -197,8 +197,13 @@ int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dty
 
 /* The first n_steps of the 2(N-1) steps (RS steps first, then AG steps) in
  * one cooperative launch, with a grid-wide barrier between consecutive
- * steps. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce.
- * Returns DDP_ENORESOURCE if the grid cannot be co-resident. A block that
+ * steps. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce. When the
+ * N buffers exceed the 256 MB Infinity Cache, each step's tiles are handed
+ * to the blocks by a ticket counter (in the launch's library-owned barrier
+ * words), so no block's fixed share holds a step back; the result does not
+ * depend on which block does which tile. Returns DDP_ENORESOURCE if the grid
+ * cannot be co-resident, DDP_EINVAL if the launch would need 2^32 tiles or
+ * more (far beyond any buffers that fit in device memory). A block that
  * waits at a barrier longer than 10 s aborts the launch (every block exits,
  * the result is incomplete) and sets a sticky flag read by
  * ddp_persistent_status. */
@@ -207,7 +212,7 @@ int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32
 
 /* As ring_allreduce_persistent, with the launch's knobs exposed:
  *   max_blocks: cooperative grid size (0: the default, 1024-thread blocks,
- *       three for every four compute units when the N buffers exceed the
+ *       seven for every eight compute units when the N buffers exceed the
  *       256 MB Infinity Cache, three for every eight when they fit); it is
  *       never more than one
  *       block per tile of a step, nor more than one block per compute unit
