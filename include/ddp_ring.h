@@ -183,7 +183,8 @@ int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* buck
 
 /* ---------------------------------------------------------------- ring all-reduce
  * bufs[N]: device pointers to the N rank buffers, `count` elements of `dtype`
- * each, aligned to the element size, pairwise disjoint. count >= 0.
+ * each, aligned to the element size, pairwise disjoint. count >= 0; with
+ * count = 0 nothing is read or written and the pointers may be NULL.
  */
 
 /* One step of the ring ([R] section 03; [X] §1.3.2.1 / §1.3.2.2): all N

@@ -38,7 +38,8 @@ inline int hip_fail(hipError_t e, const char* where) {
 // Every byte of [p, p + bytes) must lie inside one device allocation.
 int check_range(const void* p, int64_t bytes, const char* fn, const char* what);
 // N rank buffers of `bytes` each: non-NULL, aligned to `align`, inside their
-// allocations and pairwise disjoint.
+// allocations and pairwise disjoint (with bytes == 0 nothing is touched and
+// any pointer, NULL included, is accepted).
 int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, const char* fn,
                        const char* what);
 // True if every pointer is 16-byte aligned.

@@ -31,6 +31,9 @@ int check_range(const void* p, int64_t bytes, const char* fn, const char* what) 
 int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, const char* fn,
                        const char* what) {
   if (bufs == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + what + " array is NULL");
+  // Zero-length buffers are never touched: any pointer will do, NULL included
+  // (torch reports a null data pointer for an empty tensor).
+  if (bytes == 0) return DDP_OK;
   std::vector<std::pair<uintptr_t, int32_t>> spans;
   spans.reserve(n);
   for (int32_t r = 0; r < n; ++r) {
@@ -46,7 +49,7 @@ int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, c
     if (st != DDP_OK) return st;
     spans.emplace_back(reinterpret_cast<uintptr_t>(bufs[r]), r);
   }
-  if (bytes > 0) {
+  {
     std::sort(spans.begin(), spans.end());
     for (size_t i = 1; i < spans.size(); ++i) {
       if (spans[i].first - spans[i - 1].first < uint64_t(bytes))

@@ -103,6 +103,20 @@ def test_planner_argument_errors():
     expect_status(lib.ddp_plan_member(p.handle, 0, 9, None, None, None), rar.DDP_EINVAL, "out of range")
 
 
+def test_zero_count_accepts_null_buffers():
+    """count = 0 touches nothing, so NULL rank pointers (what torch reports
+    for empty tensors) are accepted and every form returns DDP_OK without a
+    launch; the pointer array itself must still exist."""
+    lib = rar.lib
+    nulls = (ctypes.c_void_p * 4)(None, None, None, None)
+    for dt in (rar.DDP_FP32, rar.DDP_BF16):
+        assert lib.ring_allreduce_fused(nulls, 4, 0, dt, None) == rar.DDP_OK
+        assert lib.ring_allreduce_step(nulls, 4, 0, dt, 1, rar.DDP_AG, None) == rar.DDP_OK
+        assert lib.ring_allreduce_persistent(nulls, 4, 0, dt, 6, None) == rar.DDP_OK
+        assert lib.ring_reduce_scatter_fused(nulls, nulls, 4, 0, dt, 0.25, None) == rar.DDP_OK
+    expect_status(lib.ring_allreduce_fused(None, 4, 0, rar.DDP_FP32, None), rar.DDP_EINVAL, "array is NULL")
+
+
 def test_ring_argument_errors_before_launch():
     lib = rar.lib
     bufs = (ctypes.c_void_p * 2)(0x1000, 0x2000)

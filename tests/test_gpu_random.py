@@ -5,6 +5,8 @@ both dtypes; and per-rank buffer starts that are 16-byte aligned, all off by
 the same amount, or mixed (some ranks aligned, some not). Each case is drawn
 once from a fixed seed, so a failure names a case that can be rerun alone."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -17,7 +19,9 @@ from gpu_util import TORCH_DTYPE, to_host, assert_bit_equal
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+# DDP_RANDOM_SCALE=k draws k times as many cases of each sweep (default 1).
+SCALE = max(1, int(os.environ.get("DDP_RANDOM_SCALE", "1")))
+N_CASES = 64 * SCALE
 
 
 def draw_cases(seed=20261202):
@@ -102,7 +106,7 @@ def test_random_case(case):
 
 # ---------------------------------------------------------------- many ranks, equal chunks
 
-N_SPAN_CASES = 16
+N_SPAN_CASES = 16 * SCALE
 
 
 def draw_span_cases(seed=20261204):
@@ -129,7 +133,7 @@ def test_random_span_case(case):
 
 # ---------------------------------------------------------------- whole DDP syncs
 
-N_SYNC_CASES = 24
+N_SYNC_CASES = 24 * SCALE
 
 
 def draw_sync_cases(seed=20261203):
