@@ -77,3 +77,27 @@ def test_n8_1gib_sampled(dtype, variant):
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_n64_300m_sampled(variant):
     sampled_check(WORKLOADS["ring_n64_300m"], "fp32", variant, k_samples=4000)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_span_beyond_cache_sampled(dtype):
+    """64 ranks x 2,560,000 elements (328 MB of bf16, 655 MB of fp32: beyond
+    the 256 MiB Infinity Cache, so the span kernel streams with non-temporal
+    loads), chunks that start mid-tile: the fused all-reduce against the
+    oracle on sampled positions, and all ranks equal everywhere."""
+    n, count = 64, 64 * 40_000
+    bufs = device_ring_inputs(64, n, count, dtype, std=1e-3)
+    pos = sample_positions(count, n, 3000, seed=64)
+    pos_dev = torch.from_numpy(pos).cuda()
+    before = [gather(t, pos_dev, dtype) for t in bufs]
+    print(f"[span {dtype}] N={n} count={count} samples={len(pos)}", flush=True)
+    rar.ring_allreduce_fused(bufs)
+    after = [gather(t, pos_dev, dtype) for t in bufs]
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    rar.ddp_count_mismatches(bufs, mism)
+    torch.cuda.synchronize()
+    assert int(mism.item()) == 0, "ranks differ after the all-reduce"
+    L = ring.chunk_length(count, n)
+    want = ring.ring_simulate(before, dtype, chunk_of=pos // L)["bufs"]
+    for r in range(n):
+        assert_bit_equal(after[r], want[r], f"span {dtype} rank {r}")
