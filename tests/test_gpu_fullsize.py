@@ -83,21 +83,36 @@ def test_n64_300m_sampled(variant):
 def test_span_beyond_cache_sampled(dtype):
     """64 ranks x 2,560,000 elements (328 MB of bf16, 655 MB of fp32: beyond
     the 256 MiB Infinity Cache, so the span kernel streams with non-temporal
-    loads), chunks that start mid-tile: the fused all-reduce against the
-    oracle on sampled positions, and all ranks equal everywhere."""
+    loads), chunks that start mid-tile: the reduce-scatter output and the
+    fused all-reduce against the oracle on sampled positions, and all ranks
+    equal everywhere after the all-reduce."""
     n, count = 64, 64 * 40_000
     bufs = device_ring_inputs(64, n, count, dtype, std=1e-3)
     pos = sample_positions(count, n, 3000, seed=64)
     pos_dev = torch.from_numpy(pos).cuda()
     before = [gather(t, pos_dev, dtype) for t in bufs]
     print(f"[span {dtype}] N={n} count={count} samples={len(pos)}", flush=True)
+    # the reduce-scatter output first (it leaves the inputs as they are): the
+    # same k offsets in every chunk form a small ring whose shards the oracle
+    # computes
+    L = ring.chunk_length(count, n)
+    rng = np.random.default_rng(65)
+    offs = np.unique(np.concatenate([rng.choice(L, 60, replace=False), [0, 1, L - 2, L - 1]]))
+    mini_pos = torch.from_numpy(np.concatenate([c * L + offs for c in range(n)])).cuda()
+    mini = [gather(t, mini_pos, dtype) for t in bufs]
+    shards = [torch.empty(L, dtype=bufs[0].dtype, device="cuda") for _ in range(n)]
+    scale = float(np.float32(1) / np.float32(n))
+    rar.ring_reduce_scatter_fused(bufs, shards, scale)
+    want_shards = ring.reduce_scatter(mini, dtype, np.float32(scale))
+    offs_dev = torch.from_numpy(offs).cuda()
+    for c in range(n):
+        assert_bit_equal(gather(shards[c], offs_dev, dtype), want_shards[c], f"span {dtype} shard {c}")
     rar.ring_allreduce_fused(bufs)
     after = [gather(t, pos_dev, dtype) for t in bufs]
     mism = torch.zeros(1, dtype=torch.int64, device="cuda")
     rar.ddp_count_mismatches(bufs, mism)
     torch.cuda.synchronize()
     assert int(mism.item()) == 0, "ranks differ after the all-reduce"
-    L = ring.chunk_length(count, n)
     want = ring.ring_simulate(before, dtype, chunk_of=pos // L)["bufs"]
     for r in range(n):
         assert_bit_equal(after[r], want[r], f"span {dtype} rank {r}")
