@@ -14,7 +14,7 @@ launch cost of the pages' 3-rank example, one default-size DDP bucket
 (8 x 25 MiB, cache-resident, and again with the cache flushed before each
 launch) in all three forms, a copy probe, the whole DDP sync of ResNet-50
 gradients (8 ranks; copying, kernel by kernel, in-place, and bf16-compressed
-both ways),
+both ways; copying and in place again with the cache flushed before each),
 the overlap of that sync with a synthetic
 backward over bucket capacities, the 64-rank 300M-element workload, and the
 CPU oracle timed on the headline workload's own inputs.
@@ -362,6 +362,16 @@ def main():
     sync["bf16_compressed_view"] = {"ms": round(t, 4),
                                     "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1),
                                     "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
+    # each sync started with the Infinity Cache flushed (a 512 MiB write outside the timed pair)
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = {}
+    for variant in ("fused", "view"):
+        bb = None if variant == "view" else buckets
+        _, med, lo = time_each(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), 20, torch,
+                               between=flush.zero_)
+        cold[variant] = {"ms_median": round(med, 4), "ms_min": round(lo, 4)}
+    sync["after_cache_flush"] = cold
+    del flush
     extras["ddp_sync_resnet50_n8"] = sync
     del buckets, cbuckets
     torch.cuda.empty_cache()
