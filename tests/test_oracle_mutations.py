@@ -15,7 +15,7 @@ from oracle import ddp, planner, ring, rounding
 from ddp_workloads import host_rank_rng, host_grads, resnet50_param_numels
 
 from test_oracle_worked_example import parse_worked_example, label_set, decode
-from test_oracle_ring import parse_order_cases
+from test_oracle_ring import parse_order_cases, parse_bound_cases, bound_case_inputs
 from test_oracle_rounding import parse_cases
 from test_oracle_planner import as_lists
 
@@ -137,8 +137,28 @@ def pin_compressed_mean():
     return True
 
 
+def pin_error_bound():
+    import torch
+    if rounding.unit_roundoff("fp32") != float(np.finfo(np.float32).eps) / 2:
+        return False
+    if rounding.unit_roundoff("bf16") != torch.finfo(torch.bfloat16).eps / 2:
+        return False
+    for case in parse_bound_cases(os.path.join(GOLDEN, "error_bound_cases.txt")):
+        dt = case["dtype"]
+        bufs = bound_case_inputs(case)
+        got = rounding.to_f64(ring.ring_simulate(bufs, dt)["bufs"][0], dt)[0]
+        bound = ring.error_bound(bufs, dt)[0]
+        err = abs(got - ring.sum_f64(bufs, dt)[0])
+        if bound != case["bound"] or err > bound:
+            return False
+        if case["attained"] and err * (1 + 2.0 ** -6) < bound:
+            return False
+    return True
+
+
 PINS = [pin_worked_example, pin_integer_sums, pin_order_fixtures, pin_traffic,
-        pin_rounding, pin_planner, pin_ddp_mean, pin_reduce_scatter, pin_compressed_mean]
+        pin_rounding, pin_planner, pin_ddp_mean, pin_reduce_scatter, pin_compressed_mean,
+        pin_error_bound]
 
 
 def test_all_pins_hold_unmutated():
@@ -176,6 +196,17 @@ def _reduce_scatter_shifted(bufs, dtype, scale=1.0):
     return shards[1:] + shards[:1]   # rank c receives chunk c+1
 
 
+_abs_sum = ring.abs_sum_f64
+
+
+def _abs_of_sum(bufs, dtype):
+    return np.abs(np.sum(np.stack([rounding.to_f64(b, dtype) for b in bufs]), axis=0))
+
+
+def _bound_with_n_terms(bufs, dtype):
+    return len(bufs) * rounding.unit_roundoff(dtype) * _abs_sum(bufs, dtype)
+
+
 MUTATIONS = {
     "rs sends the wrong chunk": (ring, "rs_chunk", lambda r, s, n: (r - s) % n),
     "ag sends the wrong chunk": (ring, "ag_chunk", lambda r, s, n: (r - 1 - s) % n),
@@ -190,6 +221,11 @@ MUTATIONS = {
     "unpack ignores the scale": (ddp, "unpack_scale", _unpack_ignoring_scale),
     "reduce-scatter ignores the scale": (ring, "reduce_scatter", _reduce_scatter_unscaled),
     "reduce-scatter gives rank c the next chunk": (ring, "reduce_scatter", _reduce_scatter_shifted),
+    "fp32 unit roundoff 2^-23": (rounding, "unit_roundoff", lambda d: 2.0 ** -23 if d == "fp32" else 2.0 ** -8),
+    "fp32 unit roundoff 2^-25": (rounding, "unit_roundoff", lambda d: 2.0 ** -25 if d == "fp32" else 2.0 ** -8),
+    "bf16 unit roundoff 2^-7": (rounding, "unit_roundoff", lambda d: 2.0 ** -24 if d == "fp32" else 2.0 ** -7),
+    "error bound on |sum g| instead of sum |g|": (ring, "abs_sum_f64", _abs_of_sum),
+    "error bound with N terms instead of N-1": (ring, "error_bound", _bound_with_n_terms),
 }
 
 

@@ -193,6 +193,68 @@ def test_error_bound_is_reached_in_part():
     assert np.all(np.abs(out - exact) <= ring.error_bound(bufs, "fp32"))
 
 
+def parse_bound_cases(path):
+    """Cases of tests/golden/error_bound_cases.txt: dtype, N, the per-rank
+    inputs and the hand-derived result, exact sum and bound (as floats)."""
+    cases, cur = [], None
+    with open(path) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            if line.startswith("case"):
+                _, dt, n = line.split()
+                cur = {"dtype": dt, "n": int(n)}
+                cases.append(cur)
+                continue
+            key, val = line.split(":", 1)
+            val = val.split()
+            if key == "ranks":
+                cur["ranks"] = [float.fromhex(v) for v in val]
+            elif key == "attained":
+                cur["attained"] = val[0] == "yes"
+            else:
+                cur[key] = float.fromhex(val[0])
+    return cases
+
+
+def bound_case_inputs(case):
+    dt = case["dtype"]
+    return [rounding.round_to(np.array([v], dtype=np.float64), dt) for v in case["ranks"]]
+
+
+def test_unit_roundoff_is_half_the_spacing_above_one():
+    """u is half the distance from 1 to the next value of the format, as numpy
+    (binary32) and torch (bfloat16) describe the formats."""
+    import torch
+    assert rounding.unit_roundoff("fp32") == float(np.finfo(np.float32).eps) / 2
+    assert rounding.unit_roundoff("bf16") == torch.finfo(torch.bfloat16).eps / 2
+
+
+def test_error_bound_golden_cases(golden_dir):
+    """Hand-derived values (tests/golden/error_bound_cases.txt): the ring's
+    result, the exact sum and the bound (N-1) u sum|g_i|; the error never
+    exceeds the bound, and in the cases built for it reaches the bound to
+    within a factor 1 + 2^-6, so a constant twice too large would show."""
+    cases = parse_bound_cases(os.path.join(golden_dir, "error_bound_cases.txt"))
+    assert len(cases) == 5
+    for case in cases:
+        dt = case["dtype"]
+        bufs = bound_case_inputs(case)
+        assert len(bufs) == case["n"]
+        out = ring.ring_simulate(bufs, dt)["bufs"]
+        got = rounding.to_f64(out[0], dt)[0]
+        assert got == case["result"], case
+        exact = ring.sum_f64(bufs, dt)[0]
+        assert exact == case["exact"], case
+        bound = ring.error_bound(bufs, dt)[0]
+        assert bound == case["bound"], case
+        err = abs(got - exact)
+        assert err <= bound
+        if case["attained"]:
+            assert err * (1 + 2.0 ** -6) >= bound, case
+
+
 def test_fsum_helper_is_exactly_rounded():
     assert ring.sum_f64([np.array([1e8], np.float32), np.array([1.0], np.float32),
                          np.array([-1e8], np.float32)], "fp32")[0] == math.fsum([1e8, 1.0, -1e8])
