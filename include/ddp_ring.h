@@ -82,7 +82,10 @@ extern "C" {
 
 typedef struct ddp_plan ddp_plan; /* opaque; host memory owned by the library */
 
-/* Message describing the last failure of the calling thread ("" if none). */
+/* Message describing the last failure of the calling thread ("" if none).
+ * Every entry point checks its arguments and reports a bad call instead of
+ * launching it: the fail-fast answer to [D] "常见疑问", where ranks that do not
+ * make matching collective calls wait forever. */
 const char* ddp_last_error(void);
 
 /* ---------------------------------------------------------------- planner
@@ -124,29 +127,34 @@ int ddp_bucket_plan_ex(const int64_t* param_numels, int32_t n_params, int32_t gr
                        int32_t comm_dtype, int64_t cap_bytes, int64_t first_bucket_bytes,
                        int32_t world_size, ddp_plan** out);
 
-/* Releases a plan and its device tables (NULL is accepted). Must not be
- * called while work that uses the plan is still running. */
+/* Releases a plan ([R] section 03 "Bucket": built once, when DDP is
+ * constructed) and its device tables (NULL is accepted). Must not be called
+ * while work that uses the plan is still running. */
 void ddp_plan_free(ddp_plan* plan);
 
-/* Number of buckets. */
+/* Number of buckets ([R] section 03 "Bucket": each is one collective). */
 int ddp_plan_num_buckets(const ddp_plan* plan, int32_t* out);
 
-/* Bucket b's padded length in elements and its number of members. */
+/* Bucket b's padded length in elements and its number of members ([R]
+ * section 03 "Bucket": the gradients of a bucket form one flat buffer). */
 int ddp_plan_bucket(const ddp_plan* plan, int32_t b, int64_t* padded_numel, int32_t* n_members);
 
 /* Member i of bucket b: parameter index, offset in the bucket (elements) and
- * element count. Members are listed in bucket order (reverse parameter order). */
+ * element count. Members are listed in bucket order, which is reverse
+ * parameter order ([R] section 03 "Overlap"). */
 int ddp_plan_member(const ddp_plan* plan, int32_t b, int32_t i, int32_t* param_idx,
                     int64_t* offset, int64_t* numel);
 
-/* Layout of a rank's gradient arena: all parameters' gradients in
+/* Layout of a rank's gradient arena (the parameters' .grad tensors that the
+ * copy back of [R] section 05 writes): all parameters' gradients in
  * registration order, parameter p starting at param_offsets[p] elements (a
  * multiple of V, i.e. 16-byte aligned). Writes *arena_numel and, if
  * param_offsets is not NULL, n_params offsets into the host array. */
 int ddp_plan_grad_arena(const ddp_plan* plan, int64_t* arena_numel, int64_t* param_offsets);
 
-/* The in-place sync's map of the gradient arena, one entry per 16-byte
- * vector of one rank's arena (n = arena_numel / V entries, written to the
+/* The in-place sync's map of the gradient arena ([R] sections 03 and 05,
+ * gradient_as_bucket_view=True: each .grad is a view of its bucket), one entry
+ * per 16-byte vector of one rank's arena (n = arena_numel / V entries, written to the
  * host array `out`): 0xFFFF for a vector holding no member element (the
  * alignment padding between parameters); otherwise the ring chunk of its
  * bucket that holds the vector (low byte) and how many of its V elements
@@ -196,9 +204,11 @@ int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* buck
 int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                         int32_t step, int32_t phase, void* stream);
 
-/* The first n_steps of the 2(N-1) steps (RS steps first, then AG steps) in
- * one cooperative launch, with a grid-wide barrier between consecutive
- * steps. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce. When the
+/* The first n_steps of the 2(N-1) steps ([X] §1.3.1: N-1 reduce-scatter
+ * steps, then N-1 all-gather steps) in one cooperative launch, with a
+ * grid-wide barrier between consecutive steps: the fixed per-step
+ * synchronisation cost of [R] section 04 (2(N-1) steps, each with its own
+ * latency) is paid inside one launch instead of at every launch. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce. When the
  * N buffers exceed the 256 MB Infinity Cache, each step's tiles are handed
  * to the blocks by a ticket counter (in the launch's library-owned barrier
  * words), so no block's fixed share holds a step back; the result does not
@@ -211,7 +221,8 @@ int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dty
 int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                               int32_t n_steps, void* stream);
 
-/* As ring_allreduce_persistent, with the launch's knobs exposed:
+/* As ring_allreduce_persistent ([X] §1.3.1; [R] section 04), with the
+ * launch's knobs exposed:
  *   max_blocks: cooperative grid size (0: the default, 1024-thread blocks,
  *       seven for every eight compute units when the N buffers exceed the
  *       256 MB Infinity Cache, three for every eight when they fit); it is
@@ -228,19 +239,23 @@ int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, in
                                  int32_t n_steps, int32_t max_blocks, int64_t timeout_us,
                                  uint32_t extra_arrivals, void* stream);
 
-/* Cooperative grid size ring_allreduce_persistent would use for these
- * arguments on the current device, and the device's compute-unit count. */
+/* Cooperative grid size ring_allreduce_persistent ([X] §1.3.1) would use
+ * for these arguments on the current device, and the device's compute-unit
+ * count. */
 int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int32_t* grid, int32_t* compute_units);
 
 /* Waits for `stream`, then reports DDP_ETIMEOUT if any persistent launch on
  * the current device timed out since the last call (and clears the flag);
- * the message gives the arrivals seen and expected at that barrier. */
+ * the message gives the arrivals seen and expected at that barrier. ([D]
+ * "常见疑问": a collective that a participant never joins waits forever; a
+ * grid barrier here gives up after its time-out and reports instead.) */
 int ddp_persistent_status(void* stream);
 
 /* The whole all-reduce in one pass: every element is read once from each of
- * the N ranks, summed in the exact order the ring adds it (chunk c's sum
- * starts with rank c+1 and adds ranks c+2, ..., c, one rounding per add) and
- * written to all N ranks. The final state is bit-identical to the 2(N-1)
+ * the N ranks, summed in the exact order the ring adds it ([X] §1.3.2.1:
+ * chunk c's sum starts with rank c+1 and adds ranks c+2, ..., c, one rounding
+ * per add) and written to all N ranks ([X] §1.3.2.2: every rank ends with the
+ * whole sum). The final state is bit-identical to the 2(N-1)
  * steps; the HBM traffic is 2*N*count*element bytes instead of
  * 5*(N-1)*count*element. */
 int ring_allreduce_fused(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
@@ -328,22 +343,29 @@ typedef struct ddp_reducer ddp_reducer;
 int ddp_reducer_create(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs, int32_t N,
                        int32_t variant, float scale, int64_t comm_max_blocks, void* comm_stream,
                        ddp_reducer** out);
+/* Releases a reducer ([R] section 03 "Overlap"); must not be called while
+ * its syncs are still running (ddp_reducer_finalize waits for them). */
 void ddp_reducer_free(ddp_reducer* reducer);
-/* Start of a backward pass: no gradient is ready. */
+/* Start of a backward pass: no gradient is ready ([R] section 05, step 2: the
+ * hooks fire as backward produces the gradients). */
 int ddp_reducer_prepare(ddp_reducer* reducer);
 /* Gradient `param` (of every rank) has been produced by work already enqueued
- * on producer_stream. If it completes its bucket, an event recorded on
+ * on producer_stream ([R] section 05, step 2: the hook of a gradient; the
+ * last one of a bucket launches its all-reduce). If it completes its bucket, an event recorded on
  * producer_stream gates that bucket's sync, which is enqueued on the
  * communication stream once every earlier bucket has been. Marking a
  * parameter twice in one pass is an error. */
 int ddp_reducer_mark_ready(ddp_reducer* reducer, int32_t param, void* producer_stream);
-/* End of backward: `stream` waits until every bucket's sync has finished.
+/* End of backward: `stream` waits until every bucket's sync has finished
+ * ([R] section 05, step 5: every bucket's all-reduce completes before the
+ * optimizer reads the gradients).
  * Returns DDP_EINVAL, naming the parameter, if some gradient was never marked
  * ready (where DDP would wait for it forever). */
 int ddp_reducer_finalize(ddp_reducer* reducer, void* stream);
 
 /* ddp_synthetic_backward: a stand-in for the backward kernels that produce
- * gradients, for overlap measurements: dsts[r][i] = srcs[r][i] for every rank
+ * gradients ([R] section 03 "Overlap": communication is hidden behind the
+ * backward computation of earlier layers), for overlap measurements: dsts[r][i] = srcs[r][i] for every rank
  * r < N and i < numel, after `work` dependent fused multiply-adds per element
  * that do not change the copied value. Each 256-thread block reserves
  * lds_kib KiB of LDS (0..64) that it never uses, which caps how many blocks
@@ -373,7 +395,8 @@ int ddp_count_mismatches(void* const* bufs, int32_t N, int64_t count, int32_t dt
 
 /* ddp_copy_probe: copies nbytes (a multiple of 16) from src to dst with 16-byte
  * vector loads and stores: a same-run reference for achievable HBM bandwidth
- * and for scaling memory-traffic counters. */
+ * (on one GPU the ring's bandwidth term of [R] section 04 is paid in HBM
+ * traffic) and for scaling memory-traffic counters. */
 int ddp_copy_probe(void* dst, const void* src, int64_t nbytes, void* stream);
 
 #ifdef __cplusplus

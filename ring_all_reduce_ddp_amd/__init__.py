@@ -15,6 +15,7 @@ library is loaded so that both use the single HIP runtime that torch ships.
 
 import ctypes
 import os
+import sys
 
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
@@ -188,6 +189,11 @@ class Plan:
             self._h = None
 
     def __del__(self):
+        # Never while the interpreter shuts down: freeing a plan's device
+        # tables calls into the HIP runtime, which may already be going away
+        # (the process's memory is returned anyway).
+        if sys.is_finalizing():
+            return
         try:
             self.free()
         except Exception:
@@ -326,9 +332,11 @@ def ring_reduce_scatter_fused(bufs, shards, scale=1.0, count=None, dtype=None, s
     _check(_get_lib().ring_reduce_scatter_fused(ptrs, sh, n, count, dt, float(scale), _stream(stream)))
 
 
-def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, stream=None):
+def ddp_sync(plan, grad_arenas, bucket_bufs=None, *, scale, variant="fused", stream=None):
     """bucket_bufs: list over buckets of lists over ranks (or a flat list,
-    bucket-major); None for the "view" variant, which uses no bucket buffers."""
+    bucket-major); None for the "view" variant, which uses no bucket buffers.
+    scale: the fp32 multiplier of the copy back, chosen by the caller (1/N
+    for DDP's mean)."""
     n = len(grad_arenas)
     if bucket_bufs is None:
         bufs = None
@@ -336,8 +344,6 @@ def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, s
         flat = [x for row in bucket_bufs for x in row] if isinstance(bucket_bufs[0], (list, tuple)) \
             else list(bucket_bufs)
         bufs = _ptr_array(flat)
-    if scale is None:
-        scale = 1.0 / n
     _check(_get_lib().ddp_sync(plan.handle, _ptr_array(grad_arenas), bufs, n, VARIANTS[variant], float(scale),
                         _stream(stream)))
 
@@ -345,9 +351,11 @@ def ddp_sync(plan, grad_arenas, bucket_bufs=None, variant="fused", scale=None, s
 class Reducer:
     """Launches each bucket's sync as soon as its last gradient is marked
     ready, on `comm_stream` (see ddp_reducer_* in include/ddp_ring.h).
-    bucket_bufs: list over buckets of lists over ranks; None for "view"."""
+    bucket_bufs: list over buckets of lists over ranks; None for "view".
+    scale: the fp32 multiplier of each bucket's copy back (1/N for DDP's
+    mean), chosen by the caller."""
 
-    def __init__(self, plan, grad_arenas, bucket_bufs=None, variant="view", scale=None, comm_stream=None,
+    def __init__(self, plan, grad_arenas, bucket_bufs=None, *, scale, variant="view", comm_stream=None,
                  comm_max_blocks=0):
         n = len(grad_arenas)
         self.plan = plan   # the plan must outlive the reducer
@@ -359,7 +367,7 @@ class Reducer:
             bufs = _ptr_array(flat)
         h = ctypes.c_void_p()
         _check(_get_lib().ddp_reducer_create(plan.handle, _ptr_array(grad_arenas), bufs, n, VARIANTS[variant],
-                                             float(1.0 / n if scale is None else scale), int(comm_max_blocks),
+                                             float(scale), int(comm_max_blocks),
                                              _stream(comm_stream), ctypes.byref(h)))
         self._h = h.value
 
@@ -378,6 +386,8 @@ class Reducer:
             self._h = None
 
     def __del__(self):
+        if sys.is_finalizing():   # as for Plan: no HIP calls during shutdown
+            return
         try:
             self.free()
         except Exception:

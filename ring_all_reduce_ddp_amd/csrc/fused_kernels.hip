@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kFusedThreads * kFusedMaxWaves) void k_fused_whole(
 // count; DDP buckets are padded and never need this): the tiles run over the
 // whole buffer from its 16-byte aligned start, so loads and stores stay
 // 16-byte vectors and staged as above, and in the sum each element takes the
-// ring order of its own chunk (a tile is never shorter than a chunk here, so
+// ring order of its own chunk (a tile is never longer than a chunk here, so
 // it crosses at most one chunk boundary). A bf16 word whose two elements lie
 // in different chunks sums each half in its own order.
 template <int DT, int NR, bool NTL>

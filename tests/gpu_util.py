@@ -35,6 +35,12 @@ def to_host(t, dtype):
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def mean_scale(n):
+    """DDP's divide-by-world-size as the fp32 multiplier fl(1/N) that the
+    caller passes to the sync entry points."""
+    return float(np.float32(1) / np.float32(n))
+
+
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint8)
 

@@ -34,6 +34,30 @@ def test_header_declares_the_entry_points():
         assert want in names
 
 
+def declaration_comments():
+    """(function name, the header text between the previous declaration and
+    this one) for every declared function: the comment that documents it."""
+    text = open(HEADER).read()
+    body = text[text.index('extern "C" {'):]
+    out, prev = [], 0
+    for m in re.finditer(r"^[a-z][^;{}()#]*?\b([a-z_][a-z0-9_]*)\s*\([^;]*\)\s*;", body, flags=re.M | re.S):
+        out.append((m.group(1), body[prev:m.start()]))
+        prev = m.end()
+    return out
+
+
+def test_every_declaration_cites_its_page():
+    """Each entry point's comment names the page passage that defines what it
+    computes: [R], [D] or [X] (the three pages listed at the top of the
+    header) with a section or part."""
+    decls = declaration_comments()
+    assert sorted(n for n, _ in decls) == declared_functions()
+    cite = re.compile(r"\[(R|D|X)\]\s*(section|§|\"|parts?|reading)")
+    flat = {n: re.sub(r"\n\s*\*\s?", " ", comment) for n, comment in decls}   # comment lines joined
+    missing = [n for n in flat if not cite.search(flat[n])]
+    assert missing == []
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(rar.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]

@@ -9,7 +9,7 @@ import ring_all_reduce_ddp_amd as rar
 from oracle import ddp, planner, ring
 from ddp_workloads import WORKLOADS, host_grads, resnet50_param_numels
 
-from gpu_util import TORCH_DTYPE, to_host, assert_bit_equal
+from gpu_util import TORCH_DTYPE, to_host, assert_bit_equal, mean_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -189,7 +189,7 @@ def test_bf16_compressed_sync(variant, n):
     grads = host_grads(60 + n, n, numels)
     arenas, offs = make_arenas(plan, grads, "fp32")
     buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
-    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+    rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=mean_scale(n))
     torch.cuda.synchronize()
     if variant == "persistent":
         rar.ddp_persistent_status()
@@ -233,7 +233,7 @@ def test_view_compressed_special_values(n):
     plan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", 4096, 256, n)
     grads = [[rng.choice(special, size=m).astype(np.float32) for m in numels] for _ in range(n)]
     arenas, offs = make_arenas(plan, grads, "fp32")
-    rar.ddp_sync(plan, arenas, None, variant="view")
+    rar.ddp_sync(plan, arenas, None, variant="view", scale=mean_scale(n))
     torch.cuda.synchronize()
     got = read_grads(arenas, offs, numels, "fp32")
     want = ddp.ddp_sync(grads, planner.plan(numels, 4, 4096, 256, n, vector_elems=8), "fp32", comm_dtype="bf16")
@@ -269,7 +269,7 @@ def test_view_sync_leaves_slack_alone(dtype):
     for a in arenas:
         a.index_fill_(0, idx, 12345.0)
     before = [to_host(a, dtype)[slack] for a in arenas]
-    rar.ddp_sync(plan, arenas, None, variant="view")
+    rar.ddp_sync(plan, arenas, None, variant="view", scale=mean_scale(n))
     torch.cuda.synchronize()
     for r, a in enumerate(arenas):
         assert_bit_equal(to_host(a, dtype)[slack], before[r], f"slack of rank {r}")
@@ -384,7 +384,7 @@ def test_bf16_resnet50_sampled(variant):
     before = [to_host(a.index_select(0, pos_dev), "bf16") for a in arenas]
     print(f"[resnet50 bf16 {variant}] arena={arena_numel} samples={len(pos)}", flush=True)
     buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
-    rar.ddp_sync(plan, arenas, buckets, variant=variant)
+    rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=mean_scale(n))
     torch.cuda.synchronize()
     if variant == "persistent":
         rar.ddp_persistent_status()

@@ -11,7 +11,7 @@ import ring_all_reduce_ddp_amd as rar
 from oracle import ddp, planner
 from ddp_workloads import host_grads, resnet50_param_numels
 
-from gpu_util import assert_bit_equal
+from gpu_util import assert_bit_equal, mean_scale
 from test_gpu_ddp import make_arenas, read_grads, bucket_buffers
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,7 @@ def test_reducer_matches_oracle(variant, order):
     n = 4
     plan, grads, arenas, offs, buckets, want = setup(variant, n)
     comm = torch.cuda.Stream()
-    red = rar.Reducer(plan, arenas, buckets, variant=variant, comm_stream=comm)
+    red = rar.Reducer(plan, arenas, buckets, variant=variant, scale=mean_scale(n), comm_stream=comm)
     params = list(range(len(NUMELS)))
     if order == "reverse":
         params.reverse()
@@ -68,7 +68,8 @@ def test_reducer_compressed_plan(variant, blocks):
     buckets = None if variant == "view" else bucket_buffers(plan, n, "bf16")
     want = ddp.ddp_sync(grads, planner.plan(NUMELS, 4, cap, first, n, vector_elems=8), "fp32", comm_dtype="bf16")
     comm = torch.cuda.Stream()
-    red = rar.Reducer(plan, arenas, buckets, variant=variant, comm_stream=comm, comm_max_blocks=blocks)
+    red = rar.Reducer(plan, arenas, buckets, variant=variant, scale=mean_scale(n), comm_stream=comm,
+                      comm_max_blocks=blocks)
     for p in reversed(range(len(NUMELS))):
         red.mark_ready(p)
     red.finalize()
@@ -79,7 +80,7 @@ def test_reducer_compressed_plan(variant, blocks):
 def test_reducer_reports_a_missing_gradient_and_recovers():
     n = 2
     plan, grads, arenas, offs, buckets, want = setup("view", n)
-    red = rar.Reducer(plan, arenas, variant="view", comm_stream=torch.cuda.Stream())
+    red = rar.Reducer(plan, arenas, variant="view", scale=mean_scale(n), comm_stream=torch.cuda.Stream())
     for p in range(len(NUMELS)):
         if p != 6:
             red.mark_ready(p)
@@ -90,7 +91,7 @@ def test_reducer_reports_a_missing_gradient_and_recovers():
     torch.cuda.synchronize()
     # a fresh pass over fresh gradients reduces everything
     arenas2, _ = make_arenas(plan, grads, "fp32")
-    red2 = rar.Reducer(plan, arenas2, variant="view", comm_stream=torch.cuda.Stream())
+    red2 = rar.Reducer(plan, arenas2, variant="view", scale=mean_scale(n), comm_stream=torch.cuda.Stream())
     red2.prepare()
     for p in reversed(range(len(NUMELS))):
         red2.mark_ready(p)
