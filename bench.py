@@ -5,7 +5,9 @@ Headline workload: 8 virtual ranks, 1 GiB of fp32 gradient per rank
 fused ring-order kernel. One step = one complete all-reduce of the 8 buffers.
 Reported: bus bandwidth 2(N-1)/N * S / t (the per-rank traffic of a ring
 all-reduce), algorithm bandwidth S / t, and the HBM bandwidth of the kernel,
-2 * N * S / t, against MI355X's 8 TB/s.
+2 * N * S / t, against MI355X's 8 TB/s. The first launch, on the pristine
+inputs and outside the timed region, is compared element by element with the
+CPU oracle's hop-by-hop ring on the same inputs (`parity`).
 
 Beside it, in the same run: the step-by-step and persistent forms, the
 reduce-scatter output alone, the same inputs in one allocation with the ranks
@@ -19,8 +21,22 @@ the overlap of that sync with a synthetic
 backward over bucket capacities, the 64-rank 300M-element workload, and the
 CPU oracle timed on the headline workload's own inputs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-Prints one JSON line.
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+      the whole benchmark; prints one JSON line.
+  python bench.py --config c1|c2|c3|c4|c5 [--variant V] [--dtype fp32|bf16]
+                  [--steps K] [--warmup W]
+      one workload and one form only (for profiling a single kernel):
+        c1  3 ranks x 6 elements    variants: fused, steps, persistent, step
+        c2  8 ranks x 25 MiB        variants: fused, steps, persistent
+        c3  ResNet-50 DDP sync, 8   variants: fused, steps, persistent, view,
+                                    pack, unpack, allreduce, bf16-fused,
+                                    bf16-view
+        c4  8 ranks x 1 GiB         variants: fused, steps, persistent,
+                                    reduce-scatter (--dtype bf16 for bf16)
+        c5  64 ranks x 300M fp32    variants: fused, steps, persistent,
+                                    reduce-scatter
+      K timed steps after W untimed ones; prints one JSON line.
 """
 
 import argparse
@@ -40,13 +56,40 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_n8_1gib_fp32.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_all_reduce_ddp_amd", "csrc", f)
                   for f in ("fused_kernels.hip", "ring_common.h", "hip_common.h")]
 
+CONFIGS = {"c1": "ring_n3_6", "c2": "ring_n8_25mib", "c3": "ddp_resnet50", "c4": "ring_n8_1gib",
+           "c5": "ring_n64_300m"}
+VARIANTS = {
+    "c1": ("fused", "steps", "persistent", "step"),
+    "c2": ("fused", "steps", "persistent"),
+    "c3": ("fused", "steps", "persistent", "view", "pack", "unpack", "allreduce", "bf16-fused", "bf16-view"),
+    "c4": ("fused", "steps", "persistent", "reduce-scatter"),
+    "c5": ("fused", "steps", "persistent", "reduce-scatter"),
+}
 
-def parse_args():
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    return ap.parse_args()
+    ap.add_argument("--config", choices=["all", *CONFIGS], default="all",
+                    help="one workload only (default: the whole benchmark)")
+    ap.add_argument("--variant", default=None, help="the form to time with --config (default: fused)")
+    ap.add_argument("--dtype", choices=["fp32", "bf16"], default="fp32", help="buffer dtype for --config c4")
+    args = ap.parse_args(argv)
+    if args.config == "all":
+        if args.variant is not None or args.dtype != "fp32":
+            ap.error("--variant and --dtype need --config")
+    else:
+        args.variant = args.variant or "fused"
+        if args.variant not in VARIANTS[args.config]:
+            ap.error(f"--variant {args.variant} is not one of {', '.join(VARIANTS[args.config])} "
+                     f"for --config {args.config}")
+        if args.dtype == "bf16" and args.config != "c4":
+            ap.error("--dtype bf16 is available for --config c4 only")
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    return args
 
 
 def ensure_library():
@@ -106,17 +149,173 @@ def traffic_from_profile():
     return prof.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: the N ranks are virtual and share one GPU; --gpus {args.gpus} is not "
-              "supported (run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def mean_scale(n, np):
+    """DDP's divide-by-world-size as the fp32 multiplier fl(1/N) of the copy back."""
+    return float(np.float32(1) / np.float32(n))
+
+
+# ---------------------------------------------------------------- workloads
+
+def ring_bytes(variant, n, S):
+    """Algorithmic HBM bytes of one all-reduce of N buffers of S bytes: the
+    fused form reads and writes every rank once (2NS); each of the 2(N-1)
+    steps reads 2 chunk-sets and writes 1 (reduce-scatter) or reads and writes
+    1 (all-gather), 5(N-1)S in all; the reduce-scatter output reads N*S and
+    writes S; one reduce-scatter step reads 2S and writes S."""
+    if variant == "fused":
+        return 2 * n * S
+    if variant in ("steps", "persistent"):
+        return 5 * (n - 1) * S
+    if variant == "reduce-scatter":
+        return (n + 1) * S
+    if variant == "step":
+        return 3 * S
+    raise ValueError(variant)
+
+
+def ring_step_fn(rar, variant, bufs, shards=None, scale=1.0):
+    if variant == "fused":
+        return lambda: rar.ring_allreduce_fused(bufs)
+    if variant == "steps":
+        return lambda: rar.ring_allreduce_stepwise(bufs)
+    if variant == "persistent":
+        return lambda: rar.ring_allreduce_persistent(bufs)
+    if variant == "step":
+        return lambda: rar.ring_allreduce_step(bufs, 0, rar.DDP_RS)
+    if variant == "reduce-scatter":
+        return lambda: rar.ring_reduce_scatter_fused(bufs, shards, scale)
+    raise ValueError(variant)
+
+
+class ResNet50Sync:
+    """The ResNet-50 DDP sync over 8 ranks: plan, gradient arenas drawn on the
+    GPU, bucket buffers (fp32, and bf16 for the compression hook)."""
+
+    def __init__(self, rar, torch, np):
+        from ddp_workloads import WORKLOADS, resnet50_param_numels
+        self.rar = rar
+        w = WORKLOADS["ddp_resnet50"]
+        self.n = w.n
+        self.numels = resnet50_param_numels()
+        self.plan = rar.ddp_bucket_plan(self.numels, "fp32", world_size=w.n)
+        self.inv_n = mean_scale(w.n, np)
+        arena_numel, _ = self.plan.grad_arena()
+        g = torch.Generator(device="cuda")
+        self.arenas = []
+        for r in range(w.n):
+            g.manual_seed(1000 * w.seed + r)
+            self.arenas.append(torch.randn(arena_numel, generator=g, device="cuda") * w.std)
+        self.buckets = [[torch.empty(self.plan.bucket(b)[0], device="cuda") for _ in range(w.n)]
+                        for b in range(self.plan.num_buckets)]
+        self.cplan = rar.ddp_bucket_plan_ex(self.numels, "fp32", "bf16", world_size=w.n)
+        self.cbuckets = [[torch.empty(self.cplan.bucket(b)[0], dtype=torch.bfloat16, device="cuda")
+                          for _ in range(w.n)] for b in range(self.cplan.num_buckets)]
+        self.grad_bytes = sum(self.numels) * 4
+
+    def fn(self, variant):
+        rar, plan = self.rar, self.plan
+        nb = plan.num_buckets
+        if variant in ("fused", "steps", "persistent"):
+            return lambda: rar.ddp_sync(plan, self.arenas, self.buckets, variant=variant, scale=self.inv_n)
+        if variant == "view":
+            return lambda: rar.ddp_sync(plan, self.arenas, None, variant="view", scale=self.inv_n)
+        if variant == "pack":
+            return lambda: [rar.bucket_pack(plan, b, self.arenas, self.buckets[b]) for b in range(nb)]
+        if variant == "unpack":
+            return lambda: [rar.bucket_unpack_scale(plan, b, self.buckets[b], self.arenas, self.inv_n)
+                            for b in range(nb)]
+        if variant == "allreduce":
+            return lambda: [rar.ring_allreduce_fused(self.buckets[b]) for b in range(nb)]
+        if variant == "bf16-fused":
+            return lambda: rar.ddp_sync(self.cplan, self.arenas, self.cbuckets, variant="fused", scale=self.inv_n)
+        if variant == "bf16-view":
+            return lambda: rar.ddp_sync(self.cplan, self.arenas, None, variant="view", scale=self.inv_n)
+        raise ValueError(variant)
+
+    def hbm_bytes(self, variant):
+        """Algorithmic bytes of the member elements (bucket padding excluded):
+        pack and unpack read and write every gradient once per rank (2NS
+        each); the copying sync adds the bucket all-reduce (2NS fused,
+        5(N-1)S by steps); the in-place sync reads and writes the gradients
+        once (2NS)."""
+        n, S = self.n, self.grad_bytes
+        return {"fused": 6 * n * S, "steps": 4 * n * S + 5 * (n - 1) * S,
+                "persistent": 4 * n * S + 5 * (n - 1) * S, "view": 2 * n * S, "pack": 2 * n * S,
+                "unpack": 2 * n * S, "allreduce": 2 * n * S, "bf16-view": 2 * n * S}.get(variant)
+
+    def free(self):
+        self.plan.free()
+        self.cplan.free()
+
+
+# ---------------------------------------------------------------- one workload, one form
+
+def run_single(args):
     ensure_library()
     import numpy as np
     import torch
     import ring_all_reduce_ddp_amd as rar
-    from ddp_workloads import WORKLOADS, device_ring_inputs, host_ring_inputs, resnet50_param_numels
+    from ddp_workloads import WORKLOADS, device_ring_inputs, host_ring_inputs
+    from ddp_workloads.gen import elements_for
+
+    torch.cuda.set_device(0)
+    cfg, variant, dtype = args.config, args.variant, args.dtype
+    w = WORKLOADS[CONFIGS[cfg]]
+    cfg_info = {"workload": w.name, "variant": variant}
+    sync = None
+    if cfg == "c3":
+        sync = ResNet50Sync(rar, torch, np)
+        fn = sync.fn(variant)
+        n, S = sync.n, sync.grad_bytes
+        hbm_bytes = sync.hbm_bytes(variant)
+        cfg_info.update({"virtual_ranks": n, "params": len(sync.numels), "grad_bytes_per_rank": S,
+                         "buckets": sync.plan.num_buckets})
+    else:
+        count = elements_for(w, dtype)
+        n = w.n
+        if cfg == "c1":
+            bufs = [torch.from_numpy(x).cuda() for x in host_ring_inputs(w.seed, w.n, w.count, "fp32", dist=w.dist)]
+        else:
+            print(f"bench: drawing {n} x {count} {dtype}", file=sys.stderr, flush=True)
+            bufs = device_ring_inputs(w.seed, n, count, dtype, std=w.std, heavy_frac=w.heavy_frac,
+                                      heavy_mult=w.heavy_mult)
+        S = count * (4 if dtype == "fp32" else 2)
+        shards = None
+        if variant == "reduce-scatter":
+            shards = [torch.empty(count // n, dtype=bufs[0].dtype, device="cuda") for _ in range(n)]
+        fn = ring_step_fn(rar, variant, bufs, shards, mean_scale(n, np))
+        hbm_bytes = ring_bytes(variant, n, S)
+        cfg_info.update({"virtual_ranks": n, "elements_per_rank": count, "bytes_per_rank": S})
+    print(f"bench: {cfg} {variant} {dtype}: {args.warmup} warm-up, {args.steps} timed", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fn()
+    ms = time_launches(fn, args.steps, torch)
+    _, med, lo = time_each(fn, args.steps, torch)
+    if variant == "persistent":
+        rar.ddp_persistent_status()
+    bus = gbps(2 * (n - 1) / n * S, ms)
+    line = {"metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": cfg_info,
+            "algbw_gbps": round(gbps(S, ms), 2), "busbw_gbps": round(bus, 2),
+            "ms_per_launch_median": round(med, 4), "ms_per_launch_min": round(lo, 4)}
+    if hbm_bytes is not None:
+        line["hbm_gbps"] = round(gbps(hbm_bytes, ms), 1)
+        line["hbm_frac_of_peak"] = round(gbps(hbm_bytes, ms) / PEAK_HBM_GBPS, 4)
+        line["algorithmic_hbm_bytes_per_step"] = hbm_bytes
+    print(json.dumps(line), flush=True)
+    if sync is not None:
+        sync.free()
+
+
+# ---------------------------------------------------------------- the whole benchmark
+
+def run_all(args):
+    ensure_library()
+    import numpy as np
+    import torch
+    import ring_all_reduce_ddp_amd as rar
+    from ddp_workloads import WORKLOADS, device_ring_inputs, host_ring_inputs
 
     torch.cuda.set_device(0)
     extras = {}
@@ -145,11 +344,8 @@ def main():
     n64_first = n64_time(lambda: rar.ring_allreduce_fused(first), 2 * w5.n * S5, 1)
     b5 = n64_inputs()
     n64 = {}
-    for name, fn, nbytes, launches in [
-            ("fused", lambda: rar.ring_allreduce_fused(b5), 2 * w5.n * S5, 1),
-            ("steps", lambda: rar.ring_allreduce_stepwise(b5), 5 * (w5.n - 1) * S5, 2 * (w5.n - 1)),
-            ("persistent", lambda: rar.ring_allreduce_persistent(b5), 5 * (w5.n - 1) * S5, 1)]:
-        n64[name] = n64_time(fn, nbytes, launches)
+    for name, launches in (("fused", 1), ("steps", 2 * (w5.n - 1)), ("persistent", 1)):
+        n64[name] = n64_time(ring_step_fn(rar, name, b5), ring_bytes(name, w5.n, S5), launches)
     # reduce-scatter output: every rank's 1/N shard of the sum (reads N*S, writes S)
     shards5 = [torch.empty(w5.count // w5.n, device="cuda") for _ in range(w5.n)]
     n64["reduce_scatter_fused"] = n64_time(lambda: rar.ring_reduce_scatter_fused(b5, shards5, 1.0 / w5.n),
@@ -170,6 +366,11 @@ def main():
     host_inputs = [t.cpu().numpy() for t in bufs]
 
     print("bench: headline fused all-reduce, 8 x 1 GiB fp32", file=sys.stderr, flush=True)
+    # The first launch runs on the pristine inputs, outside the timed region;
+    # its result is compared with the oracle's at the end.
+    rar.ring_allreduce_fused(bufs)
+    torch.cuda.synchronize()
+    first_result = [t.cpu().numpy() for t in bufs]
     for _ in range(args.warmup):
         rar.ring_allreduce_fused(bufs)
     torch.cuda.synchronize()
@@ -189,14 +390,9 @@ def main():
     # ------------------------------------------------------------ same workload, other forms
     reps = max(3, args.steps // 4)
 
-    def stepwise():
-        rar.ring_allreduce_stepwise(bufs)
-
-    def persistent():
-        rar.ring_allreduce_persistent(bufs)
-
     step_bytes = 5 * (n - 1) * S
-    for name, fn in [("steps", stepwise), ("persistent", persistent)]:
+    for name in ("steps", "persistent"):
+        fn = ring_step_fn(rar, name, bufs)
         fn()
         t = time_launches(fn, reps, torch)
         extras[name] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (n - 1) / n * S, t), 1),
@@ -255,15 +451,13 @@ def main():
     w1 = WORKLOADS["ring_n3_6"]
     b1 = [torch.from_numpy(x).cuda() for x in host_ring_inputs(w1.seed, w1.n, w1.count, "fp32", dist=w1.dist)]
     tiny = {"ranks": w1.n, "elements_per_rank": w1.count}
-    for name, fn in (("step", lambda: rar.ring_allreduce_step(b1, 0, rar.DDP_RS)),
-                     ("steps_all", lambda: rar.ring_allreduce_stepwise(b1)),
-                     ("persistent", lambda: rar.ring_allreduce_persistent(b1)),
-                     ("fused", lambda: rar.ring_allreduce_fused(b1))):
+    for name, key in (("step", "step"), ("steps", "steps_all"), ("persistent", "persistent"), ("fused", "fused")):
+        fn = ring_step_fn(rar, name, b1)
         fn()
         per_call = time_launches(fn, 1000, torch)
         _, med, lo = time_each(fn, 200, torch)
-        tiny[name] = {"us_per_call_back_to_back": round(per_call * 1e3, 2),
-                      "us_gpu_median": round(med * 1e3, 2), "us_gpu_min": round(lo * 1e3, 2)}
+        tiny[key] = {"us_per_call_back_to_back": round(per_call * 1e3, 2),
+                     "us_gpu_median": round(med * 1e3, 2), "us_gpu_min": round(lo * 1e3, 2)}
     rar.ddp_persistent_status()
     extras["ring_n3_6"] = tiny
     del b1
@@ -275,21 +469,20 @@ def main():
     b2 = device_ring_inputs(w2.seed, w2.n, w2.count, "fp32", std=w2.std)
     S2 = w2.count * 4
     bucket = {"bytes_per_rank": S2, "cache_resident": True}
-    for name, fn, nbytes in (("fused", lambda: rar.ring_allreduce_fused(b2), 2 * w2.n * S2),
-                             ("steps", lambda: rar.ring_allreduce_stepwise(b2), 5 * (w2.n - 1) * S2),
-                             ("persistent", lambda: rar.ring_allreduce_persistent(b2), 5 * (w2.n - 1) * S2)):
+    for name in ("fused", "steps", "persistent"):
+        fn = ring_step_fn(rar, name, b2)
         fn()
         t = time_launches(fn, 50, torch)
         bucket[name] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, t), 1),
-                        "algorithm_gbps": round(gbps(S2, t), 1), "hbm_gbps": round(gbps(nbytes, t), 1)}
+                        "algorithm_gbps": round(gbps(S2, t), 1),
+                        "hbm_gbps": round(gbps(ring_bytes(name, w2.n, S2), t), 1)}
     rar.ddp_persistent_status()
     # the same bucket with the Infinity Cache flushed before each launch by
     # writing a 512 MiB buffer (outside the timed region): HBM-resident inputs
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     cold = {}
-    for name, fn in (("fused", lambda: rar.ring_allreduce_fused(b2)),
-                     ("steps", lambda: rar.ring_allreduce_stepwise(b2))):
-        mean, med, lo = time_each(fn, 20, torch, between=flush.zero_)
+    for name in ("fused", "steps"):
+        mean, med, lo = time_each(ring_step_fn(rar, name, b2), 20, torch, between=flush.zero_)
         cold[name] = {"ms_median": round(med, 4), "ms_min": round(lo, 4),
                       "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, med), 1)}
     bucket["after_cache_flush"] = cold
@@ -309,71 +502,54 @@ def main():
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ whole DDP sync, ResNet-50, N=8
-    wr = WORKLOADS["ddp_resnet50"]
-    numels = resnet50_param_numels()
-    plan = rar.ddp_bucket_plan(numels, "fp32", world_size=wr.n)
-    arena_numel, _ = plan.grad_arena()
-    g = torch.Generator(device="cuda")
-    arenas = []
-    for r in range(wr.n):
-        g.manual_seed(1000 * wr.seed + r)
-        arenas.append(torch.randn(arena_numel, generator=g, device="cuda") * wr.std)
-    buckets = [[torch.empty(plan.bucket(b)[0], device="cuda") for _ in range(wr.n)]
-               for b in range(plan.num_buckets)]
-    sizes = [plan.bucket(b)[0] * 4 for b in range(plan.num_buckets)]
-    grad_bytes = sum(numels) * 4
-    sync = {"bucket_sizes": sizes, "params": len(numels), "grad_bytes_per_rank": grad_bytes}
+    rs = ResNet50Sync(rar, torch, np)
+    wr_n, grad_bytes = rs.n, rs.grad_bytes
+    sizes = [rs.plan.bucket(b)[0] * 4 for b in range(rs.plan.num_buckets)]
+    sync = {"bucket_sizes": sizes, "params": len(rs.numels), "grad_bytes_per_rank": grad_bytes}
     sync_reps = 50  # a sync takes 0.3-2 ms
     for variant in ("fused", "steps", "persistent", "view"):
-        bb = None if variant == "view" else buckets
-        rar.ddp_sync(plan, arenas, bb, variant=variant)
-        t = time_launches(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), sync_reps, torch)
-        sync[variant] = {"ms": round(t, 4),
-                         "bus_gbps": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
-        if variant in ("fused", "view"):
-            # pack + fused + unpack move 6*N*S; the in-place sync 2*N*S (padding excluded)
-            sync_bytes = (2 if variant == "view" else 6) * wr.n * grad_bytes
-            sync[variant]["hbm_gbps_algorithmic"] = round(gbps(sync_bytes, t), 1)
-    # the copying sync kernel by kernel: all packs, all fused all-reduces, all unpacks
-    nb = plan.num_buckets
-    parts = {
-        "pack": lambda: [rar.bucket_pack(plan, b, arenas, buckets[b]) for b in range(nb)],
-        "allreduce_fused": lambda: [rar.ring_allreduce_fused(buckets[b]) for b in range(nb)],
-        "unpack_scale": lambda: [rar.bucket_unpack_scale(plan, b, buckets[b], arenas, 1.0 / wr.n)
-                                 for b in range(nb)],
-    }
-    breakdown = {}
-    for name, fn in parts.items():
+        fn = rs.fn(variant)
         fn()
         t = time_launches(fn, sync_reps, torch)
-        breakdown[name] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
+        sync[variant] = {"ms": round(t, 4),
+                         "bus_gbps": round(gbps(2 * (wr_n - 1) / wr_n * grad_bytes, t), 1)}
+        if variant in ("fused", "view"):
+            # pack + fused + unpack move 6*N*S; the in-place sync 2*N*S (padding excluded)
+            sync[variant]["hbm_gbps_algorithmic"] = round(gbps(rs.hbm_bytes(variant), t), 1)
+    rar.ddp_persistent_status()
+    # the copying sync kernel by kernel: all packs, all fused all-reduces, all unpacks
+    breakdown = {}
+    for name, variant in (("pack", "pack"), ("allreduce_fused", "allreduce"), ("unpack_scale", "unpack")):
+        fn = rs.fn(variant)
+        fn()
+        t = time_launches(fn, sync_reps, torch)
+        breakdown[name] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(2 * wr_n * grad_bytes, t), 1)}
     sync["fused"]["breakdown"] = breakdown
     # the bf16 compression hook: fp32 gradients through bf16 buckets
-    cplan = rar.ddp_bucket_plan_ex(numels, "fp32", "bf16", world_size=wr.n)
-    cbuckets = [[torch.empty(cplan.bucket(b)[0], dtype=torch.bfloat16, device="cuda") for _ in range(wr.n)]
-                for b in range(cplan.num_buckets)]
-    rar.ddp_sync(cplan, arenas, cbuckets, variant="fused")
-    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, cbuckets, variant="fused"), sync_reps, torch)
+    fn = rs.fn("bf16-fused")
+    fn()
+    t = time_launches(fn, sync_reps, torch)
     sync["bf16_compressed_fused"] = {"ms": round(t, 4),
-                                     "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1)}
+                                     "bus_gbps_fp32_equivalent": round(gbps(2 * (wr_n - 1) / wr_n * grad_bytes, t), 1)}
     # the same hook in place: bf16 arithmetic on the fp32 gradients, no bf16 bucket (reads and writes 2*N*S)
-    rar.ddp_sync(cplan, arenas, None, variant="view")
-    t = time_launches(lambda: rar.ddp_sync(cplan, arenas, None, variant="view"), sync_reps, torch)
+    fn = rs.fn("bf16-view")
+    fn()
+    t = time_launches(fn, sync_reps, torch)
     sync["bf16_compressed_view"] = {"ms": round(t, 4),
-                                    "bus_gbps_fp32_equivalent": round(gbps(2 * (wr.n - 1) / wr.n * grad_bytes, t), 1),
-                                    "hbm_gbps_algorithmic": round(gbps(2 * wr.n * grad_bytes, t), 1)}
+                                    "bus_gbps_fp32_equivalent": round(gbps(2 * (wr_n - 1) / wr_n * grad_bytes, t), 1),
+                                    "hbm_gbps_algorithmic": round(gbps(2 * wr_n * grad_bytes, t), 1)}
     # each sync started with the Infinity Cache flushed (a 512 MiB write outside the timed pair)
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     cold = {}
     for variant in ("fused", "view"):
-        bb = None if variant == "view" else buckets
-        _, med, lo = time_each(lambda: rar.ddp_sync(plan, arenas, bb, variant=variant), 20, torch,
-                               between=flush.zero_)
+        _, med, lo = time_each(rs.fn(variant), 20, torch, between=flush.zero_)
         cold[variant] = {"ms_median": round(med, 4), "ms_min": round(lo, 4)}
     sync["after_cache_flush"] = cold
     del flush
     extras["ddp_sync_resnet50_n8"] = sync
-    del buckets, cbuckets
+    arenas, numels, inv_n = rs.arenas, rs.numels, rs.inv_n
+    rs.free()
+    del rs
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ overlap with a synthetic backward
@@ -387,25 +563,30 @@ def main():
     overlap = {"sync": "in place (view)", "params": len(numels), "caps": {}}
     for model, work, lds_kib in (("full_occupancy", 512, 0), ("two_waves_per_simd", 512, 64)):
         rows = {}
-        for cap_name, cap, first in (("per_gradient", 1, 1), ("6MiB", 6 << 20, 1 << 20), ("12MiB", 12 << 20, 1 << 20),
-                                     ("25MiB", 25 << 20, 1 << 20), ("50MiB", 50 << 20, 1 << 20)):
-            cplan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=cap, first_bucket_bytes=first, world_size=wr.n)
-            red = rar.Reducer(cplan, arenas, None, variant="view", comm_stream=comm)
+        for cap_name, cap, first_cap in (("per_gradient", 1, 1), ("6MiB", 6 << 20, 1 << 20),
+                                         ("12MiB", 12 << 20, 1 << 20), ("25MiB", 25 << 20, 1 << 20),
+                                         ("50MiB", 50 << 20, 1 << 20)):
+            cplan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=cap, first_bucket_bytes=first_cap,
+                                        world_size=wr_n)
+            red = rar.Reducer(cplan, arenas, None, variant="view", scale=inv_n, comm_stream=comm)
 
             def backward(mode):
                 rar.ddp_synthetic_backward_pass(cplan, srcs, arenas, work,
                                                 red if mode == "overlapped" else None, lds_kib=lds_kib,
                                                 stream=compute)
                 if mode == "sequential":
-                    rar.ddp_sync(cplan, arenas, None, variant="view", stream=compute)
+                    rar.ddp_sync(cplan, arenas, None, variant="view", scale=inv_n, stream=compute)
 
             with torch.cuda.stream(compute):
                 res = {}
                 for mode in ("backward_only", "sequential", "overlapped"):
                     backward(mode)
                     res[mode] = time_launches(lambda: backward(mode), 3, torch)
+            torch.cuda.synchronize()
+            n_buckets = cplan.num_buckets
             red.free()
-            rows[cap_name] = {"buckets": cplan.num_buckets,
+            cplan.free()
+            rows[cap_name] = {"buckets": n_buckets,
                               "backward_only_ms": round(res["backward_only"], 4),
                               "sequential_ms": round(res["sequential"], 4),
                               "overlapped_ms": round(res["overlapped"], 4),
@@ -417,13 +598,19 @@ def main():
     del arenas, srcs
     torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ CPU oracle
+    # ------------------------------------------------------------ CPU oracle, and the parity of the first launch
     print("bench: CPU oracle on the headline workload", file=sys.stderr, flush=True)
     from oracle import ring as oracle_ring
     t0 = time.perf_counter()
-    oracle_ring.ring_simulate(host_inputs, "fp32")
+    want = oracle_ring.ring_simulate(host_inputs, "fp32")["bufs"]
     cpu_s = time.perf_counter() - t0
     del host_inputs
+    mismatches = sum(int(np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32)))
+                     for got, ref in zip(first_result, want))
+    parity = {"elements": n * count, "mismatches": mismatches,
+              "against": "the CPU oracle's hop-by-hop ring on the same inputs, every element of every rank",
+              "launch": "the first fused launch, on the pristine inputs, outside the timed region"}
+    del want, first_result
     cpu = {"value": round(gbps(2 * (n - 1) / n * S, cpu_s * 1e3), 4), "unit": "GB/s",
            "cores": 1, "kind": "oracle",
            "sample": (f"the whole workload (8 ranks x {count} fp32, the same bytes the GPU reduced), "
@@ -442,6 +629,7 @@ def main():
         "hbm_frac_of_copy_probe": round(hbm / extras["copy_probe"]["gbps"], 4),
         "ms_per_launch_median": round(ms_median, 4), "ms_per_launch_min": round(ms_min, 4),
         "ranks_equal_after": ranks_equal,
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": hbm_bytes},
@@ -449,6 +637,18 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: the N ranks are virtual and share one GPU; --gpus {args.gpus} is not "
+              "supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.config == "all":
+        run_all(args)
+    else:
+        run_single(args)
 
 
 if __name__ == "__main__":

@@ -19,6 +19,42 @@ def test_more_than_one_gpu_is_refused():
     assert "--gpus 8" in proc.stderr and "one GPU" in proc.stderr
 
 
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+
+
+def test_single_config_arguments_are_checked_before_any_gpu_work():
+    """--config picks one workload and --variant one form of it; a form the
+    workload does not have, or --variant without --config, is refused by the
+    argument parser (exit status 2) before anything is imported or launched."""
+    for argv, msg in ((["--config", "c2", "--variant", "view"], "--variant view is not one of"),
+                      (["--variant", "fused"], "need --config"),
+                      (["--config", "c5", "--dtype", "bf16"], "c4 only"),
+                      (["--config", "c9"], "invalid choice"),
+                      (["--config", "c4", "--steps", "0"], "--steps must be")):
+        proc = run_bench(*argv)
+        assert proc.returncode == 2, argv
+        assert proc.stdout == ""
+        assert msg in proc.stderr, (argv, proc.stderr)
+
+
+def test_every_config_lists_its_forms():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert set(bench.CONFIGS) == {"c1", "c2", "c3", "c4", "c5"}
+    for cfg in bench.CONFIGS:
+        args = bench.parse_args(["--config", cfg])
+        assert args.variant == "fused"
+        for v in bench.VARIANTS[cfg]:
+            assert bench.parse_args(["--config", cfg, "--variant", v]).variant == v
+    assert bench.parse_args([]).config == "all"
+    # algorithmic bytes: the fused form moves 2NS, the step forms 5(N-1)S
+    assert bench.ring_bytes("fused", 8, 1 << 30) == 16 << 30
+    assert bench.ring_bytes("steps", 8, 1 << 30) == 35 << 30
+    assert bench.ring_bytes("reduce-scatter", 8, 1 << 30) == 9 << 30
+
+
 def test_traffic_figure_follows_the_kernel_sources():
     """bench.py reports the counter-based HBM bytes only while the fused
     kernel's sources hash to the value the counters were taken on."""
