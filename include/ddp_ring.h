@@ -239,6 +239,23 @@ int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, in
                                  int32_t n_steps, int32_t max_blocks, int64_t timeout_us,
                                  uint32_t extra_arrivals, void* stream);
 
+/* ring_allreduce_persistent_noalloc: ring_allreduce_persistent for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, kernels
+ * and results; the launch's barrier words live in a fixed 512-byte array
+ * that the library holds in device memory from load time (one per GPU, until
+ * the process ends), so no call allocates: no hipMalloc, no hipFree, no
+ * allocating library routine. The array is one launch's worth and its size
+ * does not depend on the inputs, so no input size is refused for it (the
+ * limits are those of ring_allreduce_persistent). Every call on a GPU shares
+ * that GPU's array: the barrier words are cleared on `stream` before each
+ * launch, so calls on one stream are ordered, but calls that overlap on one
+ * GPU (other streams, other host threads) race on the words and must not be
+ * made. A barrier time-out sets the array's sticky status, which
+ * ddp_persistent_status reports and clears. */
+int ring_allreduce_persistent_noalloc(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                                      int32_t n_steps, void* stream);
+
 /* Cooperative grid size ring_allreduce_persistent ([X] §1.3.1) would use
  * for these arguments on the current device, and the device's compute-unit
  * count. */

@@ -72,6 +72,7 @@ def _load():
         "ring_allreduce_step": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, vp]),
         "ring_allreduce_persistent": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
         "ring_allreduce_persistent_ex": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, i64, ctypes.c_uint32, vp]),
+        "ring_allreduce_persistent_noalloc": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
         "ddp_persistent_grid": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "ddp_persistent_status": (ctypes.c_int, [vp]),
         "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
@@ -301,6 +302,15 @@ def ring_allreduce_persistent_ex(bufs, n_steps=None, max_blocks=0, timeout_us=10
         n_steps = 2 * (n - 1)
     _check(_get_lib().ring_allreduce_persistent_ex(ptrs, n, count, dt, int(n_steps), int(max_blocks),
                                             int(timeout_us), int(extra_arrivals), _stream(stream)))
+
+
+def ring_allreduce_persistent_noalloc(bufs, n_steps=None, count=None, dtype=None, stream=None):
+    """ring_allreduce_persistent with its barrier words in the library's fixed
+    device array instead of an allocation (calls on one GPU must not overlap)."""
+    ptrs, n, count, dt = _ring_args(bufs, count, dtype)
+    if n_steps is None:
+        n_steps = 2 * (n - 1)
+    _check(_get_lib().ring_allreduce_persistent_noalloc(ptrs, n, count, dt, int(n_steps), _stream(stream)))
 
 
 def ddp_persistent_grid(n, count, dtype="fp32"):

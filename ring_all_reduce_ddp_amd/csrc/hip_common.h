@@ -49,6 +49,11 @@ bool all_aligned16(void* const* bufs, int32_t n);
 // a device pointer to 64 32-bit words reserved for one launch, zeroed
 // on `stream` ahead of it; *status the device's sticky timeout word.
 int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status);
+// Zeroes n 32-bit words at p on `stream` with a fill kernel (runtime.hip).
+int zero_words(unsigned int* p, int n, hipStream_t stream);
+// The status words of the allocation-free persistent launches on device
+// `dev`, or NULL if none has run there (ring_kernels.hip).
+unsigned int* noalloc_status_words(int dev);
 
 // The in-place sync of bucket b on arenas already checked by
 // check_view_arenas, with at most max_blocks blocks (0: as many as tiles)

@@ -25,6 +25,7 @@
 // element by element, this chunk's elements only. No LDS and no matrix
 // cores: nothing here is reused across threads or shaped like a contraction.
 #include <algorithm>
+#include <mutex>
 
 #include "ring_common.h"
 
@@ -240,6 +241,39 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
   }
 }
 
+// ---------------------------------------------------------------- allocation-free scratch
+
+// Barrier words of ring_allreduce_persistent_noalloc, for callers that cannot
+// allocate device memory: words [0, 64) are one launch's barrier slot
+// (arrivals in word 0, tile tickets in word kTicketWord), words [64, 67) its
+// sticky status (timed out, arrivals seen, arrivals expected). 512 bytes per
+// device, zero when the code object is loaded, held until the process ends.
+constexpr int kNoAllocSlotWords = 64;
+constexpr int kNoAllocWords = 128;
+static __device__ __align__(256) unsigned int scratch[kNoAllocWords];
+
+// The device address of `scratch` on each device. In host code the array's
+// name is only a stand-in for the symbol; the address comes from
+// hipGetSymbolAddress, fetched once per device with that device current.
+std::mutex g_noalloc_mu;
+unsigned int* g_noalloc_words[kMaxDevices] = {};
+
+int noalloc_scratch(unsigned int** out) {
+  int dev = 0;
+  DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DDP_EINVAL, "ring_allreduce_persistent_noalloc: device index beyond 64");
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_words[dev] == nullptr) {
+    void* p = nullptr;
+    DDP_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                "ring_allreduce_persistent_noalloc: hipGetSymbolAddress");
+    g_noalloc_words[dev] = static_cast<unsigned int*>(p);
+  }
+  *out = g_noalloc_words[dev];
+  return DDP_OK;
+}
+
 // ---------------------------------------------------------------- host side
 
 // Tiles per chunk of the persistent kernel (256 threads x kStepUnroll vectors).
@@ -275,6 +309,7 @@ struct PersistentOpts {
   int32_t max_blocks = 0;       // 0: the default grid (see persistent_grid)
   int64_t timeout_us = kDefaultTimeoutUs;
   uint32_t extra_arrivals = 0;  // test hook: forces the time-out path
+  bool noalloc = false;         // barrier words in the file-scope scratch, not library allocations
 };
 
 // Grid of the persistent kernel: the default above for the buffers' cache
@@ -321,8 +356,18 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
               "ring_allreduce_persistent: wall clock rate");
   unsigned int* slot = nullptr;
   unsigned int* status = nullptr;
-  st = barrier_slot(s, &slot, &status);
-  if (st != DDP_OK) return st;
+  if (o.noalloc) {
+    unsigned int* words = nullptr;
+    st = noalloc_scratch(&words);
+    if (st != DDP_OK) return st;
+    st = zero_words(words, kNoAllocSlotWords, s);  // the status words stay: they are sticky
+    if (st != DDP_OK) return st;
+    slot = words;
+    status = words + kNoAllocSlotWords;
+  } else {
+    st = barrier_slot(s, &slot, &status);
+    if (st != DDP_OK) return st;
+  }
   RankPtrs P = a.P;
   int n = a.n;
   int64_t count = a.count, L = a.L, tiles = tpc;
@@ -364,6 +409,13 @@ int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int3
 }
 
 }  // namespace
+
+unsigned int* noalloc_status_words(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  return g_noalloc_words[dev] == nullptr ? nullptr : g_noalloc_words[dev] + kNoAllocSlotWords;
+}
+
 }  // namespace ddp
 
 using namespace ddp;
@@ -385,6 +437,13 @@ extern "C" int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, 
 extern "C" int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                          int32_t n_steps, void* stream) {
   return persistent("ring_allreduce_persistent", bufs, N, count, dtype, n_steps, PersistentOpts{}, stream);
+}
+
+extern "C" int ring_allreduce_persistent_noalloc(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
+                                                 int32_t n_steps, void* stream) {
+  PersistentOpts o;
+  o.noalloc = true;
+  return persistent("ring_allreduce_persistent_noalloc", bufs, N, count, dtype, n_steps, o, stream);
 }
 
 extern "C" int ddp_persistent_grid(int32_t N, int64_t count, int32_t dtype, int32_t* grid,

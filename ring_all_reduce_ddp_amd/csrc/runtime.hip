@@ -9,54 +9,63 @@
 
 namespace ddp {
 
-int check_range(const void* p, int64_t bytes, const char* fn, const char* what) {
+namespace {
+
+// "what" or "what[index]" (index >= 0): built only for a failure message, so a
+// successful check allocates no host memory.
+std::string name_of(const char* what, int32_t index) {
+  return index < 0 ? std::string(what) : std::string(what) + "[" + std::to_string(index) + "]";
+}
+
+int check_range_at(const void* p, int64_t bytes, const char* fn, const char* what, int32_t index) {
   if (bytes == 0) return DDP_OK;
-  if (p == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + what + " is NULL");
+  if (p == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, index) + " is NULL");
   hipDeviceptr_t base = nullptr;
   size_t size = 0;
   hipError_t e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return fail(DDP_EINVAL, std::string(fn) + ": " + what +
+    return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, index) +
                                 " is not inside a device allocation of this process");
   }
   const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
   const uintptr_t q = reinterpret_cast<uintptr_t>(p);
   if (q < lo || uint64_t(bytes) > size || q - lo > size - uint64_t(bytes))
-    return fail(DDP_EINVAL, std::string(fn) + ": " + what + " range of " + std::to_string(bytes) +
+    return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, index) + " range of " + std::to_string(bytes) +
                                 " bytes runs past the end of its allocation");
   return DDP_OK;
+}
+
+}  // namespace
+
+int check_range(const void* p, int64_t bytes, const char* fn, const char* what) {
+  return check_range_at(p, bytes, fn, what, -1);
 }
 
 int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, const char* fn,
                        const char* what) {
   if (bufs == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + what + " array is NULL");
+  if (n < 1 || n > DDP_MAX_RANKS) return fail(DDP_EINVAL, std::string(fn) + ": N must lie in [1, 64]");
   // Zero-length buffers are never touched: any pointer will do, NULL included
   // (torch reports a null data pointer for an empty tensor).
   if (bytes == 0) return DDP_OK;
-  std::vector<std::pair<uintptr_t, int32_t>> spans;
-  spans.reserve(n);
   for (int32_t r = 0; r < n; ++r) {
-    const std::string name = std::string(what) + "[" + std::to_string(r) + "]";
-    if (bufs[r] == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is NULL");
+    if (bufs[r] == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, r) + " is NULL");
     if (reinterpret_cast<uintptr_t>(bufs[r]) % uintptr_t(align) != 0)
-      return fail(DDP_EINVAL, std::string(fn) + ": " + name + " is not " + std::to_string(align) +
+      return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, r) + " is not " + std::to_string(align) +
                                   "-byte aligned");
   }
+  std::pair<uintptr_t, int32_t> spans[DDP_MAX_RANKS];
   for (int32_t r = 0; r < n; ++r) {
-    const std::string name = std::string(what) + "[" + std::to_string(r) + "]";
-    int st = check_range(bufs[r], bytes, fn, name.c_str());
+    int st = check_range_at(bufs[r], bytes, fn, what, r);
     if (st != DDP_OK) return st;
-    spans.emplace_back(reinterpret_cast<uintptr_t>(bufs[r]), r);
+    spans[r] = {reinterpret_cast<uintptr_t>(bufs[r]), r};
   }
-  {
-    std::sort(spans.begin(), spans.end());
-    for (size_t i = 1; i < spans.size(); ++i) {
-      if (spans[i].first - spans[i - 1].first < uint64_t(bytes))
-        return fail(DDP_EINVAL, std::string(fn) + ": " + what + "[" +
-                                    std::to_string(spans[i - 1].second) + "] and " + what + "[" +
-                                    std::to_string(spans[i].second) + "] overlap");
-    }
+  std::sort(spans, spans + n);
+  for (int32_t i = 1; i < n; ++i) {
+    if (spans[i].first - spans[i - 1].first < uint64_t(bytes))
+      return fail(DDP_EINVAL, std::string(fn) + ": " + name_of(what, spans[i - 1].second) + " and " +
+                                  name_of(what, spans[i].second) + " overlap");
   }
   return DDP_OK;
 }
@@ -114,15 +123,21 @@ int device_scratch(DeviceScratch** out) {
 
 }  // namespace
 
+int zero_words(unsigned int* p, int n, hipStream_t stream) {
+  // A fill kernel rather than a memset node keeps this usable under graph capture.
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, stream, p, n);
+  DDP_HIP_TRY(hipGetLastError(), "barrier words: zero launch");
+  return DDP_OK;
+}
+
 int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status) {
   DeviceScratch* s = nullptr;
   int st = device_scratch(&s);
   if (st != DDP_OK) return st;
   const unsigned int k = s->next.fetch_add(1u) % kSlots;
   unsigned int* p = s->words + size_t(k) * kSlotStride;
-  // A fill kernel rather than a memset node keeps this usable under graph capture.
-  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, stream, p, kSlotStride);
-  DDP_HIP_TRY(hipGetLastError(), "barrier words: zero launch");
+  st = zero_words(p, kSlotStride, stream);
+  if (st != DDP_OK) return st;
   *slot = p;
   *status = s->words + size_t(kSlots) * kSlotStride;
   return DDP_OK;
@@ -259,21 +274,30 @@ extern "C" int ddp_synthetic_backward(const void* const* srcs, void* const* dsts
 }
 
 extern "C" int ddp_persistent_status(void* stream) {
-  DeviceScratch* s = nullptr;
-  int st = device_scratch(&s);
-  if (st != DDP_OK) return st;
+  int dev = 0;
+  DDP_HIP_TRY(hipGetDevice(&dev), "ddp_persistent_status: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "ddp_persistent_status: device index beyond 64");
   DDP_HIP_TRY(hipStreamSynchronize(as_stream(stream)), "ddp_persistent_status: hipStreamSynchronize");
-  unsigned int* status = s->words + size_t(kSlots) * kSlotStride;
-  unsigned int host[3] = {0, 0, 0};
-  DDP_HIP_TRY(hipMemcpy(host, status, sizeof(host), hipMemcpyDeviceToHost),
-              "ddp_persistent_status: hipMemcpy");
-  if (host[0] != 0) {
-    const unsigned int zero[3] = {0, 0, 0};
-    DDP_HIP_TRY(hipMemcpy(status, zero, sizeof(zero), hipMemcpyHostToDevice),
+  // The status words of the launches with library-allocated barrier words
+  // (if any was made on this device) and of the allocation-free ones.
+  unsigned int* lines[2] = {nullptr, noalloc_status_words(dev)};
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev].words != nullptr) lines[0] = g_scratch[dev].words + size_t(kSlots) * kSlotStride;
+  }
+  for (unsigned int* status : lines) {
+    if (status == nullptr) continue;
+    unsigned int host[3] = {0, 0, 0};
+    DDP_HIP_TRY(hipMemcpy(host, status, sizeof(host), hipMemcpyDeviceToHost),
                 "ddp_persistent_status: hipMemcpy");
-    return fail(DDP_ETIMEOUT, "ring_allreduce_persistent: a grid barrier timed out with " +
-                                  std::to_string(host[1]) + " of " + std::to_string(host[2]) +
-                                  " block arrivals; results are incomplete");
+    if (host[0] != 0) {
+      const unsigned int zero[3] = {0, 0, 0};
+      DDP_HIP_TRY(hipMemcpy(status, zero, sizeof(zero), hipMemcpyHostToDevice),
+                  "ddp_persistent_status: hipMemcpy");
+      return fail(DDP_ETIMEOUT, "ring_allreduce_persistent: a grid barrier timed out with " +
+                                    std::to_string(host[1]) + " of " + std::to_string(host[2]) +
+                                    " block arrivals; results are incomplete");
+    }
   }
   return DDP_OK;
 }
