@@ -120,6 +120,8 @@ def sync_case(variant, n, dtype, numels, cap, first, seed, scale=None, comm=None
         grads_f32 = grads
     arenas, offs = make_arenas(plan, grads_f32, dtype)
     buckets = None if variant == "view" else bucket_buffers(plan, n, comm or dtype)
+    if scale is None:
+        scale = mean_scale(n)
     rar.ddp_sync(plan, arenas, buckets, variant=variant, scale=scale)
     torch.cuda.synchronize()
     if variant == "persistent":
