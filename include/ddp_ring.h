@@ -208,7 +208,11 @@ int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, int32_t dty
  * steps, then N-1 all-gather steps) in one cooperative launch, with a
  * grid-wide barrier between consecutive steps: the fixed per-step
  * synchronisation cost of [R] section 04 (2(N-1) steps, each with its own
- * latency) is paid inside one launch instead of at every launch. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce. When the
+ * latency) is paid inside one launch instead of at every launch. The barrier
+ * words come from 64 slots per device, handed out in turn; a launch that
+ * reuses a slot first makes its stream wait (on the GPU, not the host) for
+ * the slot's previous user, whatever stream that was on. Not for graph
+ * capture: use ring_allreduce_persistent_noalloc there. n_steps in [0, 2(N-1)]; 2(N-1) is the whole all-reduce. When the
  * N buffers exceed the 256 MB Infinity Cache, each step's tiles are handed
  * to the blocks by a ticket counter (in the launch's library-owned barrier
  * words), so no block's fixed share holds a step back; the result does not
@@ -255,6 +259,16 @@ int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, in
  * ddp_persistent_status reports and clears. */
 int ring_allreduce_persistent_noalloc(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                       int32_t n_steps, void* stream);
+
+/* ddp_persistent_test_hook: for tests of the time-out path only ([D]
+ * "常见疑问": a collective that a participant never joins waits forever; here
+ * it gives up and reports). With timeout_us > 0, every later persistent
+ * launch of the process that takes default options (ring_allreduce_persistent,
+ * its _noalloc form, and ddp_sync and the reducer with DDP_VARIANT_PERSISTENT)
+ * expects extra_arrivals more blocks at each grid barrier and gives up after
+ * timeout_us; timeout_us = 0 restores the defaults (10 s, no extra arrivals).
+ * timeout_us in [0, 3600 s]. */
+int ddp_persistent_test_hook(uint32_t extra_arrivals, int64_t timeout_us);
 
 /* Cooperative grid size ring_allreduce_persistent ([X] §1.3.1) would use
  * for these arguments on the current device, and the device's compute-unit
@@ -320,7 +334,10 @@ int ring_reduce_scatter_fused(const void* const* bufs, void* const* shards, int3
  * ddp_sync: one DDP gradient synchronisation. For every bucket b in plan
  * order: bucket_pack, the all-reduce chosen by `variant` (DDP_VARIANT_FUSED,
  * _STEPS or _PERSISTENT) on bucket b's N buffers, bucket_unpack_scale with
- * `scale` (pass 1/N for DDP's mean). Bucket i+1 is never started before
+ * `scale` (pass 1/N for DDP's mean). With DDP_VARIANT_PERSISTENT, a bucket
+ * whose all-reduce gives up at a grid barrier (ring_allreduce_persistent) is
+ * not copied back: its gradients keep their values, and ddp_persistent_status
+ * reports DDP_ETIMEOUT once the stream has reached it. Bucket i+1 is never started before
  * bucket i ([R] section 03). For DDP_VARIANT_VIEW the gradients themselves
  * are reduced in place, all buckets in one launch over the arenas (every
  * bucket is ready when ddp_sync is called): each element is summed in its
@@ -375,7 +392,9 @@ int ddp_reducer_prepare(ddp_reducer* reducer);
 int ddp_reducer_mark_ready(ddp_reducer* reducer, int32_t param, void* producer_stream);
 /* End of backward: `stream` waits until every bucket's sync has finished
  * ([R] section 05, step 5: every bucket's all-reduce completes before the
- * optimizer reads the gradients).
+ * optimizer reads the gradients). With DDP_VARIANT_PERSISTENT a bucket whose
+ * all-reduce timed out keeps its gradients (see ddp_sync); check
+ * ddp_persistent_status after this stream is done.
  * Returns DDP_EINVAL, naming the parameter, if some gradient was never marked
  * ready (where DDP would wait for it forever). */
 int ddp_reducer_finalize(ddp_reducer* reducer, void* stream);

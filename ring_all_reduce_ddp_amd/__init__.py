@@ -73,6 +73,7 @@ def _load():
         "ring_allreduce_persistent": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
         "ring_allreduce_persistent_ex": (ctypes.c_int, [pp, i32, i64, i32, i32, i32, i64, ctypes.c_uint32, vp]),
         "ring_allreduce_persistent_noalloc": (ctypes.c_int, [pp, i32, i64, i32, i32, vp]),
+        "ddp_persistent_test_hook": (ctypes.c_int, [ctypes.c_uint32, i64]),
         "ddp_persistent_grid": (ctypes.c_int, [i32, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "ddp_persistent_status": (ctypes.c_int, [vp]),
         "ring_allreduce_fused": (ctypes.c_int, [pp, i32, i64, i32, vp]),
@@ -311,6 +312,12 @@ def ring_allreduce_persistent_noalloc(bufs, n_steps=None, count=None, dtype=None
     if n_steps is None:
         n_steps = 2 * (n - 1)
     _check(_get_lib().ring_allreduce_persistent_noalloc(ptrs, n, count, dt, int(n_steps), _stream(stream)))
+
+
+def ddp_persistent_test_hook(extra_arrivals=0, timeout_us=0):
+    """Tests of the time-out path only: later default persistent launches
+    expect extra_arrivals more blocks and give up after timeout_us (0 resets)."""
+    _check(_get_lib().ddp_persistent_test_hook(int(extra_arrivals), int(timeout_us)))
 
 
 def ddp_persistent_grid(n, count, dtype="fp32"):

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <string>
 
+#include "barrier_slots.h"
 #include "ddp_internal.h"
 
 namespace ddp {
@@ -45,10 +46,58 @@ int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, c
 // True if every pointer is 16-byte aligned.
 bool all_aligned16(void* const* bufs, int32_t n);
 
-// Per-device persistent-barrier words (defined in runtime.hip): *slot receives
-// a device pointer to 64 32-bit words reserved for one launch, zeroed
-// on `stream` ahead of it; *status the device's sticky timeout word.
-int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status);
+// Per-device persistent-barrier words (defined in runtime.hip). A lease holds
+// one of the device's slots of 64 32-bit words: barrier_acquire makes
+// `stream` wait for the slot's previous user's work (see barrier_slots.h),
+// then zeroes the words on `stream`; `status` is the device's sticky timeout
+// line. barrier_release records the end of the lease's work on `stream` and
+// frees the slot; it must follow every successful barrier_acquire, after
+// everything that reads the words (a kernel that checks the abort bit
+// included) has been enqueued.
+struct BarrierLease {
+  unsigned int* words = nullptr;
+  unsigned int* status = nullptr;
+  int slot = -1;
+  int dev = -1;
+};
+int barrier_acquire(hipStream_t stream, BarrierLease* lease);
+int barrier_release(BarrierLease* lease, hipStream_t stream);
+
+// Releases a held lease when it goes out of scope (on an early error return).
+class BarrierGuard {
+ public:
+  explicit BarrierGuard(hipStream_t s) : s_(s) {}
+  BarrierGuard(const BarrierGuard&) = delete;
+  BarrierGuard& operator=(const BarrierGuard&) = delete;
+  ~BarrierGuard() { (void)barrier_release(&lease_, s_); }
+  int acquire() { return barrier_acquire(s_, &lease_); }
+  int release() { return barrier_release(&lease_, s_); }
+  unsigned int* words() const { return lease_.words; }
+  unsigned int* status() const { return lease_.status; }
+
+ private:
+  hipStream_t s_;
+  BarrierLease lease_;
+};
+
+// The top bit of a persistent launch's arrival word: set when a grid barrier
+// gave up waiting (the launch's result is incomplete).
+constexpr unsigned int kAbortBit = 0x80000000u;
+
+// The whole persistent all-reduce (2(N-1) steps) with barrier words that the
+// caller leased and that are zero (ring_kernels.hip).
+int persistent_allreduce_leased(void* const* bufs, int32_t N, int64_t count, int32_t dtype, unsigned int* words,
+                                unsigned int* status, hipStream_t s);
+// bucket_unpack_scale on checked arguments, skipped by every block if
+// `abort_word` is not NULL and has kAbortBit set when the kernel runs: the
+// copy back of a persistent all-reduce that gave up leaves the gradients as
+// they were (pack_kernels.hip).
+int unpack_scale_guarded(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs, void* const* grad_arenas,
+                         int32_t N, float scale, const unsigned int* abort_word, hipStream_t s);
+// pack, persistent all-reduce, guarded unpack of bucket b under one lease
+// (pack_kernels.hip; used by ddp_sync and the reducer).
+int sync_bucket_persistent(const ddp_plan* plan, int32_t b, void* const* grad_arenas, void* const* bucket_bufs,
+                           int32_t N, float scale, hipStream_t s);
 // Zeroes n 32-bit words at p on `stream` with a fill kernel (runtime.hip).
 int zero_words(unsigned int* p, int n, hipStream_t stream);
 // The status words of the allocation-free persistent launches on device

@@ -72,10 +72,19 @@ __global__ __launch_bounds__(kThreads) void k_pack(const Segment* segs, const in
 // copying sync 0.79 against 0.83 ms with cached stores). Pack keeps cached
 // stores: the all-reduce that follows reads the bucket from the cache
 // (streaming them made the same sync 0.90 ms).
+// True if the persistent all-reduce whose arrival word this is gave up (a
+// NULL word: no such all-reduce precedes this copy back).
+__device__ __forceinline__ bool aborted(const unsigned int* abort_word) {
+  return abort_word != nullptr &&
+         (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kAbortBit) != 0u;
+}
+
 template <int DT, bool NTS>
 __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
-                                                           RankPtrs buckets, RankPtrs arenas, float scale) {
+                                                           RankPtrs buckets, RankPtrs arenas, float scale,
+                                                           const unsigned int* abort_word) {
   using O = Ops<DT>;
+  if (aborted(abort_word)) return;  // leave the gradients as they were
   constexpr int V = O::V;
   constexpr int U = kPackVecsPerThread;
   constexpr int64_t kTile = int64_t(kThreads) * U * V;
@@ -155,7 +164,9 @@ __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* se
 // (non-temporal ones made the compressed ResNet-50 sync over 8 ranks 0.75 ms
 // against 0.66).
 __global__ __launch_bounds__(kThreads) void k_unpack_bf16_to_f32(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
-                                                                 RankPtrs buckets, RankPtrs arenas, float scale) {
+                                                                 RankPtrs buckets, RankPtrs arenas, float scale,
+                                                                 const unsigned int* abort_word) {
+  if (aborted(abort_word)) return;  // leave the gradients as they were
   constexpr int V = 8;
   constexpr int U = kPackVecsPerThread;
   constexpr int64_t kTile = int64_t(kThreads) * U * V;
@@ -311,16 +322,15 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   return DDP_OK;
 }
 
-extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs,
-                                   void* const* grad_arenas, int32_t N, float scale, void* stream) {
-  const char* fn = "bucket_unpack_scale";
-  int st = check_copy(fn, plan, b, grad_arenas, bucket_bufs, N);
-  if (st != DDP_OK) return st;
+namespace ddp {
+
+int unpack_scale_guarded(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs, void* const* grad_arenas,
+                         int32_t N, float scale, const unsigned int* abort_word, hipStream_t s) {
   const Bucket& bk = plan->buckets[b];
   if (bk.n_tiles == 0) return DDP_OK;
   const Segment* segs = nullptr;
   const int32_t* tile_seg = nullptr;
-  st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr, &tile_seg);
+  int st = device_tables(const_cast<ddp_plan*>(plan), &segs, nullptr, &tile_seg);
   if (st != DDP_OK) return st;
   RankPtrs A{}, B{};
   for (int r = 0; r < N; ++r) {
@@ -328,28 +338,55 @@ extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* 
     B.p[r] = const_cast<void*>(bucket_bufs[r]);
   }
   const dim3 g(copy_grid(bk.n_tiles), unsigned(N)), blk(kThreads);
-  hipStream_t s = as_stream(stream);
   const Segment* sg = segs + bk.seg_begin;
   const int32_t* ts = tile_seg + bk.tile_seg_begin;
   // Non-temporal stores (same-dtype plans) once the N gradient arenas
   // together exceed the Infinity Cache: they would not stay cached for a
   // consumer anyway.
   const bool nts = int64_t(N) * plan->arena_numel * elem_bytes(plan->dtype) > kInfinityCacheBytes;
+  const float sc = scale;
   if (plan->dtype != plan->comm_dtype) {
-    hipLaunchKernelGGL(k_unpack_bf16_to_f32, g, blk, 0, s, sg, ts, bk.n_tiles, B, A, scale);
+    hipLaunchKernelGGL(k_unpack_bf16_to_f32, g, blk, 0, s, sg, ts, bk.n_tiles, B, A, sc, abort_word);
   } else if (plan->dtype == DDP_FP32) {
     if (nts)
-      hipLaunchKernelGGL((k_unpack_scale<DDP_FP32, true>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, scale);
+      hipLaunchKernelGGL((k_unpack_scale<DDP_FP32, true>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, sc, abort_word);
     else
-      hipLaunchKernelGGL((k_unpack_scale<DDP_FP32, false>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, scale);
+      hipLaunchKernelGGL((k_unpack_scale<DDP_FP32, false>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, sc, abort_word);
   } else {
     if (nts)
-      hipLaunchKernelGGL((k_unpack_scale<DDP_BF16, true>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, scale);
+      hipLaunchKernelGGL((k_unpack_scale<DDP_BF16, true>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, sc, abort_word);
     else
-      hipLaunchKernelGGL((k_unpack_scale<DDP_BF16, false>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, scale);
+      hipLaunchKernelGGL((k_unpack_scale<DDP_BF16, false>), g, blk, 0, s, sg, ts, bk.n_tiles, B, A, sc, abort_word);
   }
   DDP_HIP_TRY(hipGetLastError(), "bucket_unpack_scale: launch");
   return DDP_OK;
+}
+
+int sync_bucket_persistent(const ddp_plan* plan, int32_t b, void* const* grad_arenas, void* const* bufs, int32_t N,
+                           float scale, hipStream_t s) {
+  // bucket_pack checks the arenas and buffers that the copy back uses too
+  int st = bucket_pack(plan, b, const_cast<const void* const*>(grad_arenas), bufs, N, s);
+  if (st != DDP_OK) return st;
+  // One lease covers the all-reduce and the copy back, which reads the
+  // launch's abort bit: the slot is not handed on before both have run.
+  BarrierGuard lease(s);
+  st = lease.acquire();
+  if (st != DDP_OK) return st;
+  st = persistent_allreduce_leased(bufs, N, plan->buckets[b].padded_numel, plan->comm_dtype, lease.words(),
+                                   lease.status(), s);
+  if (st != DDP_OK) return st;
+  st = unpack_scale_guarded(plan, b, const_cast<const void* const*>(bufs), grad_arenas, N, scale, lease.words(), s);
+  if (st != DDP_OK) return st;
+  return lease.release();
+}
+
+}  // namespace ddp
+
+extern "C" int bucket_unpack_scale(const ddp_plan* plan, int32_t b, const void* const* bucket_bufs,
+                                   void* const* grad_arenas, int32_t N, float scale, void* stream) {
+  int st = check_copy("bucket_unpack_scale", plan, b, grad_arenas, bucket_bufs, N);
+  if (st != DDP_OK) return st;
+  return unpack_scale_guarded(plan, b, bucket_bufs, grad_arenas, N, scale, nullptr, as_stream(stream));
 }
 
 extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* const* bucket_bufs,
@@ -375,12 +412,16 @@ extern "C" int ddp_sync(const ddp_plan* plan, void* const* grad_arenas, void* co
   for (int32_t b = 0; b < int32_t(plan->buckets.size()); ++b) {
     void* const* bufs = bucket_bufs + size_t(b) * N;
     const int64_t count = plan->buckets[b].padded_numel;
+    if (variant == DDP_VARIANT_PERSISTENT) {
+      // a persistent all-reduce that times out leaves the gradients unchanged
+      int st = sync_bucket_persistent(plan, b, grad_arenas, bufs, N, scale, as_stream(stream));
+      if (st != DDP_OK) return st;
+      continue;
+    }
     int st = bucket_pack(plan, b, const_cast<const void* const*>(grad_arenas), bufs, N, stream);
     if (st != DDP_OK) return st;
     if (variant == DDP_VARIANT_FUSED) {
       st = ring_allreduce_fused(bufs, N, count, plan->comm_dtype, stream);
-    } else if (variant == DDP_VARIANT_PERSISTENT) {
-      st = ring_allreduce_persistent(bufs, N, count, plan->comm_dtype, 2 * (N - 1), stream);
     } else {
       for (int ph = DDP_RS; ph <= DDP_AG && st == DDP_OK; ++ph)
         for (int s = 0; s + 1 < N && st == DDP_OK; ++s)

@@ -63,12 +63,12 @@ int launch_bucket(ddp_reducer* r, int32_t b) {
   }
   void* const* bufs = r->bucket_bufs.data() + size_t(b) * r->n;
   const int64_t count = plan->buckets[b].padded_numel;
+  if (r->variant == DDP_VARIANT_PERSISTENT)  // a time-out leaves the gradients unchanged
+    return ddp::sync_bucket_persistent(plan, b, r->arenas.data(), bufs, r->n, r->scale, r->comm);
   int st = bucket_pack(plan, b, const_cast<const void* const*>(r->arenas.data()), bufs, r->n, s);
   if (st != DDP_OK) return st;
   if (r->variant == DDP_VARIANT_FUSED) {
     st = ring_allreduce_fused(bufs, r->n, count, plan->comm_dtype, s);
-  } else if (r->variant == DDP_VARIANT_PERSISTENT) {
-    st = ring_allreduce_persistent(bufs, r->n, count, plan->comm_dtype, 2 * (r->n - 1), s);
   } else {
     for (int ph = DDP_RS; ph <= DDP_AG && st == DDP_OK; ++ph)
       for (int k = 0; k + 1 < r->n && st == DDP_OK; ++k)

@@ -25,6 +25,7 @@
 // element by element, this chunk's elements only. No LDS and no matrix
 // cores: nothing here is reused across threads or shaped like a contraction.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "ring_common.h"
@@ -142,7 +143,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(RankPtrs P, int n, int64_
 
 // ---------------------------------------------------------------- persistent
 
-constexpr unsigned kAbortBit = 0x80000000u;
 // Word of a launch's barrier slot (64 words, zeroed before the launch) that
 // holds the tile-ticket counter: its own 128-byte line, away from the
 // arrival counter in word 0 that waiting blocks poll.
@@ -305,11 +305,31 @@ int launch_step(const RingArgs& a, int step, int phase, hipStream_t s) {
   return nt ? launch_step_impl<DT, false, true>(a, step, phase, s) : launch_step_impl<DT, false, false>(a, step, phase, s);
 }
 
+// Test hook (ddp_persistent_test_hook): when set, the persistent launches that
+// take default options expect this many more arrivals at every barrier and
+// give up after this many microseconds, so tests can drive the time-out path
+// of ddp_sync and the reducer from the host.
+std::atomic<uint32_t> g_hook_extra{0};
+std::atomic<int64_t> g_hook_timeout_us{0};
+
 struct PersistentOpts {
   int32_t max_blocks = 0;       // 0: the default grid (see persistent_grid)
   int64_t timeout_us = kDefaultTimeoutUs;
   uint32_t extra_arrivals = 0;  // test hook: forces the time-out path
   bool noalloc = false;         // barrier words in the file-scope scratch, not library allocations
+  unsigned int* words = nullptr;   // barrier words leased (and zeroed) by the caller, if not NULL
+  unsigned int* status = nullptr;  // with `words`: the status line of the lease
+
+  // Default options, or the test hook's if it is set.
+  static PersistentOpts defaults() {
+    PersistentOpts o;
+    const int64_t t = g_hook_timeout_us.load();
+    if (t > 0) {
+      o.timeout_us = t;
+      o.extra_arrivals = g_hook_extra.load();
+    }
+    return o;
+  }
 };
 
 // Grid of the persistent kernel: the default above for the buffers' cache
@@ -356,7 +376,11 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
               "ring_allreduce_persistent: wall clock rate");
   unsigned int* slot = nullptr;
   unsigned int* status = nullptr;
-  if (o.noalloc) {
+  BarrierGuard lease(s);  // barrier words leased here, unless the caller holds them
+  if (o.words != nullptr) {
+    slot = o.words;
+    status = o.status;
+  } else if (o.noalloc) {
     unsigned int* words = nullptr;
     st = noalloc_scratch(&words);
     if (st != DDP_OK) return st;
@@ -365,8 +389,10 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
     slot = words;
     status = words + kNoAllocSlotWords;
   } else {
-    st = barrier_slot(s, &slot, &status);
+    st = lease.acquire();
     if (st != DDP_OK) return st;
+    slot = lease.words();
+    status = lease.status();
   }
   RankPtrs P = a.P;
   int n = a.n;
@@ -382,7 +408,7 @@ int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts&
     return fail(DDP_ENORESOURCE, "ring_allreduce_persistent: grid cannot be co-resident");
   }
   if (e != hipSuccess) return hip_fail(e, "ring_allreduce_persistent: hipLaunchCooperativeKernel");
-  return DDP_OK;
+  return lease.release();
 }
 
 int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int32_t dtype, int32_t n_steps,
@@ -410,6 +436,14 @@ int persistent(const char* fn, void* const* bufs, int32_t N, int64_t count, int3
 
 }  // namespace
 
+int persistent_allreduce_leased(void* const* bufs, int32_t N, int64_t count, int32_t dtype, unsigned int* words,
+                                unsigned int* status, hipStream_t s) {
+  PersistentOpts o = PersistentOpts::defaults();
+  o.words = words;
+  o.status = status;
+  return persistent("ring_allreduce_persistent", bufs, N, count, dtype, N >= 1 ? 2 * (N - 1) : 0, o, s);
+}
+
 unsigned int* noalloc_status_words(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_noalloc_mu);
@@ -436,12 +470,20 @@ extern "C" int ring_allreduce_step(void* const* bufs, int32_t N, int64_t count, 
 
 extern "C" int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                          int32_t n_steps, void* stream) {
-  return persistent("ring_allreduce_persistent", bufs, N, count, dtype, n_steps, PersistentOpts{}, stream);
+  return persistent("ring_allreduce_persistent", bufs, N, count, dtype, n_steps, PersistentOpts::defaults(), stream);
+}
+
+extern "C" int ddp_persistent_test_hook(uint32_t extra_arrivals, int64_t timeout_us) {
+  if (timeout_us < 0 || timeout_us > int64_t(3600) * 1000000)
+    return fail(DDP_EINVAL, "ddp_persistent_test_hook: timeout_us must lie in [0, 3600 s]");
+  g_hook_extra.store(timeout_us > 0 ? extra_arrivals : 0u);
+  g_hook_timeout_us.store(timeout_us);
+  return DDP_OK;
 }
 
 extern "C" int ring_allreduce_persistent_noalloc(void* const* bufs, int32_t N, int64_t count, int32_t dtype,
                                                  int32_t n_steps, void* stream) {
-  PersistentOpts o;
+  PersistentOpts o = PersistentOpts::defaults();
   o.noalloc = true;
   return persistent("ring_allreduce_persistent_noalloc", bufs, N, count, dtype, n_steps, o, stream);
 }

@@ -80,14 +80,33 @@ bool all_aligned16(void* const* bufs, int32_t n) {
 
 namespace {
 
-constexpr int kSlots = 64;          // launches that may be in flight at once per device
+constexpr int kSlots = 64;          // slots handed out round-robin per device
 constexpr int kSlotStride = 64;     // words between slots (256 bytes); a launch uses word 0 (barrier
                                     // arrivals) and word 32 (the persistent kernel's tile tickets)
 constexpr int kScratchWords = kSlots * kSlotStride + kSlotStride;  // + status line
 
+// HIP events for SlotRing: a slot's next user waits, on its own stream, for
+// the event its previous user recorded after its work on the slot.
+struct HipSlotOps {
+  using Event = hipEvent_t;
+  using Stream = hipStream_t;
+  static int create(Event* e) {
+    const hipError_t err = hipEventCreateWithFlags(e, hipEventDisableTiming);
+    return err == hipSuccess ? DDP_OK : hip_fail(err, "barrier words: hipEventCreateWithFlags");
+  }
+  static int wait(Stream s, Event e) {
+    const hipError_t err = hipStreamWaitEvent(s, e, 0);
+    return err == hipSuccess ? DDP_OK : hip_fail(err, "barrier words: hipStreamWaitEvent");
+  }
+  static int record(Event e, Stream s) {
+    const hipError_t err = hipEventRecord(e, s);
+    return err == hipSuccess ? DDP_OK : hip_fail(err, "barrier words: hipEventRecord");
+  }
+};
+
 struct DeviceScratch {
   unsigned int* words = nullptr;    // kScratchWords words; the last line holds the status
-  std::atomic<unsigned int> next{0};
+  SlotRing<kSlots, HipSlotOps> ring;
 };
 
 std::mutex g_scratch_mu;
@@ -97,7 +116,7 @@ __global__ void k_zero_words(unsigned int* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
-int device_scratch(DeviceScratch** out) {
+int device_scratch(int* dev_out, DeviceScratch** out) {
   int dev = 0;
   DDP_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(DDP_EINVAL, "device index beyond 64");
@@ -117,6 +136,7 @@ int device_scratch(DeviceScratch** out) {
     }
     s.words = static_cast<unsigned int*>(p);
   }
+  *dev_out = dev;
   *out = &s;
   return DDP_OK;
 }
@@ -130,17 +150,30 @@ int zero_words(unsigned int* p, int n, hipStream_t stream) {
   return DDP_OK;
 }
 
-int barrier_slot(hipStream_t stream, unsigned int** slot, unsigned int** status) {
+int barrier_acquire(hipStream_t stream, BarrierLease* lease) {
   DeviceScratch* s = nullptr;
-  int st = device_scratch(&s);
+  int dev = 0;
+  int st = device_scratch(&dev, &s);
   if (st != DDP_OK) return st;
-  const unsigned int k = s->next.fetch_add(1u) % kSlots;
-  unsigned int* p = s->words + size_t(k) * kSlotStride;
-  st = zero_words(p, kSlotStride, stream);
+  SlotRing<kSlots, HipSlotOps>::Lease l;
+  st = s->ring.acquire(stream, &l);
   if (st != DDP_OK) return st;
-  *slot = p;
-  *status = s->words + size_t(kSlots) * kSlotStride;
-  return DDP_OK;
+  lease->dev = dev;
+  lease->slot = l.slot;
+  lease->words = s->words + size_t(l.slot) * kSlotStride;
+  lease->status = s->words + size_t(kSlots) * kSlotStride;
+  st = zero_words(lease->words, kSlotStride, stream);
+  if (st != DDP_OK) (void)barrier_release(lease, stream);
+  return st;
+}
+
+int barrier_release(BarrierLease* lease, hipStream_t stream) {
+  if (lease->slot < 0) return DDP_OK;
+  SlotRing<kSlots, HipSlotOps>::Lease l;
+  l.slot = lease->slot;
+  l.ring = &g_scratch[lease->dev].ring;
+  lease->slot = -1;
+  return l.ring->release(&l, stream);
 }
 
 // ---------------------------------------------------------------- all-ranks-equal count

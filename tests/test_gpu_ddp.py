@@ -400,3 +400,46 @@ def test_bf16_resnet50_sampled(variant):
     want = ddp.unpack_scale(reduced, flat, np.float32(1) / np.float32(n), "bf16")[0]
     for r in range(n):
         assert_bit_equal(after[r], want, f"{variant} rank {r}")
+
+
+@pytest.mark.parametrize("path", ["ddp_sync", "reducer"])
+def test_persistent_timeout_leaves_gradients(path):
+    """A persistent all-reduce that gives up at a grid barrier (forced from the
+    host: every barrier expects one block more than the grid has, 20 ms
+    deadline) is not copied back: every gradient keeps its bits, the status
+    call reports the time-out, and a normal sync afterwards equals the
+    oracle's."""
+    numels = [7, 16, 1, 40, 3, 300, 9, 5000, 33]
+    n = 4
+    plan = rar.ddp_bucket_plan(numels, "fp32", cap_bytes=4096, first_bucket_bytes=64, world_size=n)
+    assert plan.num_buckets > 1
+    grads = host_grads(91, n, numels)
+    arenas, offs = make_arenas(plan, grads, "fp32")
+    buckets = bucket_buffers(plan, n, "fp32")
+    before = [to_host(a, "fp32") for a in arenas]
+    print(f"[persistent time-out via {path}] buckets={plan.num_buckets}", flush=True)
+    rar.ddp_persistent_test_hook(extra_arrivals=1, timeout_us=20_000)
+    try:
+        if path == "ddp_sync":
+            rar.ddp_sync(plan, arenas, buckets, variant="persistent", scale=mean_scale(n))
+        else:
+            red = rar.Reducer(plan, arenas, buckets, variant="persistent", scale=mean_scale(n),
+                              comm_stream=torch.cuda.Stream())
+            for p in reversed(range(len(numels))):
+                red.mark_ready(p)
+            red.finalize()
+        torch.cuda.synchronize()
+    finally:
+        rar.ddp_persistent_test_hook(0, 0)
+    with pytest.raises(rar.DDPError, match="timed out"):
+        rar.ddp_persistent_status()
+    for r in range(n):
+        assert_bit_equal(to_host(arenas[r], "fp32"), before[r], f"{path}: rank {r} after the time-out")
+    rar.ddp_sync(plan, arenas, buckets, variant="persistent", scale=mean_scale(n))
+    torch.cuda.synchronize()
+    rar.ddp_persistent_status()
+    want = ddp.ddp_sync(grads, planner.plan(numels, 4, 4096, 64, n), "fp32")
+    got = read_grads(arenas, offs, numels, "fp32")
+    for r in range(n):
+        for p in range(len(numels)):
+            assert_bit_equal(got[r][p], want[r][p], f"{path}: after recovery, rank {r} param {p}")

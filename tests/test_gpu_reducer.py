@@ -100,7 +100,7 @@ def test_reducer_reports_a_missing_gradient_and_recovers():
     check(arenas2, offs, NUMELS, want, n, "second pass")
 
 
-@pytest.mark.parametrize("variant", ["view", "fused"])
+@pytest.mark.parametrize("variant", ["view", "fused", "persistent"])
 def test_overlapped_backward_resnet50(variant):
     """Synthetic backward (reverse parameter order) on one stream, buckets
     reduced on another as they fill: the result equals the oracle's sync of
@@ -122,6 +122,8 @@ def test_overlapped_backward_resnet50(variant):
             red.mark_ready(p, stream=compute)
         red.finalize(stream=compute)
     torch.cuda.synchronize()
+    if variant == "persistent":
+        rar.ddp_persistent_status()
     want = ddp.ddp_sync(grads, planner.plan(numels, 4, 12 * 2 ** 20, 2 ** 20, n), "fp32", scale=0.125)
     check(arenas, offs, numels, want, n, f"overlapped {variant}")
 

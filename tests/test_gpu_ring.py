@@ -302,3 +302,28 @@ def test_persistent_tickets_timeout_path(big_inputs):
     want = ring.ring_simulate(big_inputs, "fp32")["bufs"]
     for r in range(BIG_N):
         assert_bit_equal(to_host(dev[r], "fp32"), want[r], f"after a time-out, rank {r}")
+
+
+def test_persistent_slots_reused_across_two_streams():
+    """130 persistent launches queued on two streams behind long-running
+    kernels, so all are in flight at once and the device's 64 barrier slots
+    are each handed out two or three times, alternately to launches on the two
+    streams (20 launches on one, then 20 on the other). A slot's next user
+    waits for its previous user: every result equals the oracle's."""
+    n, count, k = 4, 4 * 2000 + 3, 130
+    hosts = [host_ring_inputs(500 + i, n, count, "fp32") for i in range(k)]
+    devs = [to_device(h, "fp32") for h in hosts]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    src = [torch.randn(65536, device="cuda") for _ in range(2)]
+    dst = [torch.empty_like(t) for t in src]
+    torch.cuda.synchronize()
+    for st in streams:   # ~10 ms of dependent arithmetic at the head of each stream
+        rar.ddp_synthetic_backward(src, dst, work=3_000_000, stream=st)
+    for i in range(k):
+        rar.ring_allreduce_persistent(devs[i], stream=streams[(i // 20) % 2])
+    torch.cuda.synchronize()
+    rar.ddp_persistent_status()
+    for i in range(k):
+        want = ring.ring_simulate(hosts[i], "fp32")["bufs"]
+        for r in range(n):
+            assert_bit_equal(to_host(devs[i][r], "fp32"), want[r], f"launch {i} rank {r}")
