@@ -25,7 +25,7 @@ Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W]
       the whole benchmark; prints one JSON line.
   python bench.py --config c1|c2|c3|c4|c5 [--variant V] [--dtype fp32|bf16]
-                  [--steps K] [--warmup W]
+                  [--graph] [--steps K] [--warmup W]
       one workload and one form only (for profiling a single kernel):
         c1  3 ranks x 6 elements    variants: fused, steps, persistent, step
         c2  8 ranks x 25 MiB        variants: fused, steps, persistent
@@ -36,7 +36,9 @@ Usage:
                                     reduce-scatter (--dtype bf16 for bf16)
         c5  64 ranks x 300M fp32    variants: fused, steps, persistent,
                                     reduce-scatter
-      K timed steps after W untimed ones; prints one JSON line.
+      K timed steps after W untimed ones (--graph: replays of a HIP graph of
+      one step, so no host work sits between its launches); prints one JSON
+      line.
 """
 
 import argparse
@@ -76,10 +78,12 @@ def parse_args(argv=None):
                     help="one workload only (default: the whole benchmark)")
     ap.add_argument("--variant", default=None, help="the form to time with --config (default: fused)")
     ap.add_argument("--dtype", choices=["fp32", "bf16"], default="fp32", help="buffer dtype for --config c4")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --config: time replays of a HIP graph of one step instead of eager calls")
     args = ap.parse_args(argv)
     if args.config == "all":
-        if args.variant is not None or args.dtype != "fp32":
-            ap.error("--variant and --dtype need --config")
+        if args.variant is not None or args.dtype != "fp32" or args.graph:
+            ap.error("--variant, --dtype and --graph need --config")
     else:
         args.variant = args.variant or "fused"
         if args.variant not in VARIANTS[args.config]:
@@ -87,6 +91,8 @@ def parse_args(argv=None):
                      f"for --config {args.config}")
         if args.dtype == "bf16" and args.config != "c4":
             ap.error("--dtype bf16 is available for --config c4 only")
+        if args.graph and args.variant == "persistent":
+            ap.error("--graph: the persistent form orders its barrier words with events; time it eagerly")
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
     return args
@@ -131,6 +137,23 @@ def time_each(fn, reps, torch, between=None):
 
 def gbps(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def graph_of(fn, torch):
+    """fn()'s launches captured in a HIP graph (after one eager call, which
+    makes a plan's device tables on first use): replaying it runs them back to
+    back with no host work between them."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s, capture_error_mode="thread_local"):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
 
 
 def traffic_from_profile():
@@ -286,7 +309,11 @@ def run_single(args):
         fn = ring_step_fn(rar, variant, bufs, shards, mean_scale(n, np))
         hbm_bytes = ring_bytes(variant, n, S)
         cfg_info.update({"virtual_ranks": n, "elements_per_rank": count, "bytes_per_rank": S})
-    print(f"bench: {cfg} {variant} {dtype}: {args.warmup} warm-up, {args.steps} timed", file=sys.stderr, flush=True)
+    print(f"bench: {cfg} {variant} {dtype}: {args.warmup} warm-up, {args.steps} timed"
+          f"{' (graph replays)' if args.graph else ''}", file=sys.stderr, flush=True)
+    if args.graph:
+        fn = graph_of(fn, torch).replay
+        cfg_info["graph_replay"] = True
     for _ in range(args.warmup):
         fn()
     ms = time_launches(fn, args.steps, torch)
@@ -487,6 +514,15 @@ def run_all(args):
                       "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, med), 1)}
     bucket["after_cache_flush"] = cold
     del flush
+    # the 14 step launches and the fused launch replayed from a HIP graph: no host work between launches
+    replayed = {}
+    for name in ("fused", "steps"):
+        g = graph_of(ring_step_fn(rar, name, b2), torch)
+        t = time_launches(g.replay, 50, torch)
+        replayed[name] = {"ms": round(t, 4), "bus_gbps": round(gbps(2 * (w2.n - 1) / w2.n * S2, t), 1),
+                          "hbm_gbps": round(gbps(ring_bytes(name, w2.n, S2), t), 1)}
+        del g
+    bucket["graph_replay"] = replayed
     extras["ring_n8_25mib"] = bucket
     del b2
     torch.cuda.empty_cache()
@@ -525,6 +561,16 @@ def run_all(args):
         t = time_launches(fn, sync_reps, torch)
         breakdown[name] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(2 * wr_n * grad_bytes, t), 1)}
     sync["fused"]["breakdown"] = breakdown
+    # The same syncs replayed from HIP graphs (every launch of the sync captured
+    # once): no host work between launches; on this stack a replay is not
+    # faster than the eager calls, which already keep the GPU busy.
+    replayed = {}
+    for variant in ("fused", "view"):
+        g = graph_of(rs.fn(variant), torch)
+        t = time_launches(g.replay, sync_reps, torch)
+        replayed[variant] = {"ms": round(t, 4), "hbm_gbps_algorithmic": round(gbps(rs.hbm_bytes(variant), t), 1)}
+        del g
+    sync["graph_replay"] = replayed
     # the bf16 compression hook: fp32 gradients through bf16 buckets
     fn = rs.fn("bf16-fused")
     fn()

@@ -190,11 +190,12 @@ class Plan:
             _get_lib().ddp_plan_free(self._h)
             self._h = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # Never while the interpreter shuts down: freeing a plan's device
         # tables calls into the HIP runtime, which may already be going away
-        # (the process's memory is returned anyway).
-        if sys.is_finalizing():
+        # (the process's memory is returned anyway). The check is bound at
+        # definition: module globals such as `sys` may already be None here.
+        if _finalizing():
             return
         try:
             self.free()
@@ -402,8 +403,8 @@ class Reducer:
             _get_lib().ddp_reducer_free(self._h)
             self._h = None
 
-    def __del__(self):
-        if sys.is_finalizing():   # as for Plan: no HIP calls during shutdown
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if _finalizing():   # as for Plan: no HIP calls during shutdown
             return
         try:
             self.free()

@@ -32,7 +32,9 @@ def test_single_config_arguments_are_checked_before_any_gpu_work():
                       (["--variant", "fused"], "need --config"),
                       (["--config", "c5", "--dtype", "bf16"], "c4 only"),
                       (["--config", "c9"], "invalid choice"),
-                      (["--config", "c4", "--steps", "0"], "--steps must be")):
+                      (["--config", "c4", "--steps", "0"], "--steps must be"),
+                      (["--graph"], "need --config"),
+                      (["--config", "c2", "--variant", "persistent", "--graph"], "time it eagerly")):
         proc = run_bench(*argv)
         assert proc.returncode == 2, argv
         assert proc.stdout == ""
