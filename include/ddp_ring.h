@@ -246,7 +246,7 @@ int ring_allreduce_persistent_ex(void* const* bufs, int32_t N, int64_t count, in
 /* ring_allreduce_persistent_noalloc: ring_allreduce_persistent for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc). Same arguments, kernels
- * and results; the launch's barrier words live in a fixed 512-byte array
+ * and results; the launch's barrier words live in a fixed 1 KiB array
  * that the library holds in device memory from load time (one per GPU, until
  * the process ends), so no call allocates: no hipMalloc, no hipFree, no
  * allocating library routine. The array is one launch's worth and its size

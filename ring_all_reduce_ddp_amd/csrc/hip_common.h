@@ -47,7 +47,7 @@ int check_rank_buffers(void* const* bufs, int32_t n, int64_t bytes, int align, c
 bool all_aligned16(void* const* bufs, int32_t n);
 
 // Per-device persistent-barrier words (defined in runtime.hip). A lease holds
-// one of the device's slots of 64 32-bit words: barrier_acquire makes
+// one of the device's slots of kSlotWords 32-bit words: barrier_acquire makes
 // `stream` wait for the slot's previous user's work (see barrier_slots.h),
 // then zeroes the words on `stream`; `status` is the device's sticky timeout
 // line. barrier_release records the end of the lease's work on `stream` and
@@ -83,6 +83,9 @@ class BarrierGuard {
 // The top bit of a persistent launch's arrival word: set when a grid barrier
 // gave up waiting (the launch's result is incomplete).
 constexpr unsigned int kAbortBit = 0x80000000u;
+// 32-bit words in one launch's barrier slot (three 128-byte lines in use; see
+// ring_kernels.hip).
+constexpr int kSlotWords = 128;
 
 // The whole persistent all-reduce (2(N-1) steps) with barrier words that the
 // caller leased and that are zero (ring_kernels.hip).

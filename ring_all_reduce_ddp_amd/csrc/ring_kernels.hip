@@ -36,21 +36,20 @@ namespace {
 constexpr int kStepUnroll = 4;    // 16-byte vectors per thread in a step tile
 constexpr int64_t kDefaultTimeoutUs = 10 * 1000 * 1000;  // grid barrier patience: 10 s
 // Persistent grid, measured on MI355X (14 steps, 8 ranks): 1024-thread blocks.
-// Buffers beyond the Infinity Cache (8 x 1 GiB fp32), tiles handed out by
-// tickets: seven blocks for every eight compute units (224): 5.91-5.94 ms;
-// 128, 160, 192 and 256 blocks took 7.63, 6.78, 6.15 and 5.97 ms (64 ranks x
-// 300M: 61.5 ms at 192, 59.8 at 256). With a fixed grid-stride share per
-// block instead, 192 blocks were best at 6.52 ms (160 to 256: 6.65, 6.54,
-// 6.52, 6.77, 6.96, 7.08, 7.23 ms): a step ended when its slowest block did.
-// Buffers inside it (cached accesses): three blocks
-// for every eight compute units (96): 8 x 25 MiB 0.287 ms against 0.344 ms
-// with 192 (16, 32, 64, 128 blocks: 0.756, 0.430, 0.304, 0.295 ms); 8 x 16
-// MiB 0.217 against 0.271 ms. More blocks add barrier arrivals, polling and,
-// with cached stores, write-backs of dirty cache lines at every barrier;
-// fewer leave bandwidth unused.
+// Buffers beyond the Infinity Cache, tiles handed out by tickets: seven
+// blocks for every eight compute units (224). With the split barrier whose
+// waiters poll a release word, 8 x 256 MiB fp32 took 1.62 ms at 224 blocks
+// (16 to 256 blocks: 11.8, 6.09, 3.25, 2.36, 2.02, 1.80, 1.67, 1.62, 1.64 ms).
+// Buffers inside it (cached accesses, a fixed share per block): five blocks
+// for every eight compute units (160), rounded so that every block has the
+// same number of tiles per step (a step ends when its slowest block does):
+// 8 x 25 MiB took 0.248 ms at 160 blocks (16 to 256: 0.771, 0.433, 0.286,
+// 0.257, 0.256, 0.248, 0.268, 0.258, 0.273 ms). Fewer blocks leave bandwidth
+// unused; more add barrier arrivals and, with cached stores, write-backs of
+// dirty cache lines at every barrier.
 constexpr int kPersistentThreads = 1024;   // threads per persistent block
 constexpr int kPersistentBlocksPer8CUsStreaming = 7;
-constexpr int kPersistentBlocksPer8CUsCached = 3;
+constexpr int kPersistentBlocksPer8CUsCached = 5;
 
 // ---------------------------------------------------------------- one step
 
@@ -126,6 +125,97 @@ __device__ __forceinline__ void step_tile(const RankPtrs& P, int n, int64_t coun
   }
 }
 
+// The vector form of one tile, in two halves, so that a loop over tiles can
+// issue the next tile's loads before the current tile's stores: within a step
+// no tile reads what another tile of the step writes (transfer r writes chunk
+// (r-1-s) of rank r+1, which only transfer r itself reads), so the order of
+// one tile's stores and another's loads does not matter.
+template <int U>
+struct StagedTile {
+  u32x4 a[U], b[U];  // sent operand, and the receiver's own (reduce-scatter only)
+  int64_t base = 0, lo = 0, hi = 0;  // the tile's first element; the chunk's range
+  int r = 0;                          // the sending rank
+};
+
+// Where tile `tile` of step s lies: sending rank, chunk range, first element.
+template <int DT, int T, int U>
+__device__ __forceinline__ void step_tile_place(int n, int64_t count, int64_t L, int64_t tiles_per_chunk,
+                                                int64_t tile, int s, int phase, StagedTile<U>& t) {
+  constexpr int64_t kTile = int64_t(T) * U * Ops<DT>::V;
+  t.r = int(tile / tiles_per_chunk);
+  const int c = step_chunk(t.r, s, n, phase);
+  t.lo = int64_t(c) * L;
+  t.hi = min(t.lo + L, count);
+  t.base = (t.lo / kTile + (tile - int64_t(t.r) * tiles_per_chunk)) * kTile;
+}
+
+// The sent operand (rank r's copy of the chunk), whole vectors only.
+template <int DT, int T, int U, bool NT>
+__device__ __forceinline__ void step_tile_load_sent(const RankPtrs& P, StagedTile<U>& t) {
+  constexpr int V = Ops<DT>::V;
+  if (t.base >= t.hi) return;
+  const u32x4* src = static_cast<const u32x4*>(P.p[t.r]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t vi = t.base / V + int64_t(u) * T + threadIdx.x;
+    if (vi * V >= t.lo && (vi + 1) * V <= t.hi) t.a[u] = ld16<NT>(src + vi);
+  }
+}
+
+// The receiver's own copy of the chunk, which a reduce-scatter step adds to.
+// In reduce-scatter step s it has not been written by any earlier step (rank
+// r+1 receives chunk (r-1-s) in step s and in no other reduce-scatter step),
+// so it may be loaded before the barrier that ends step s-1 completes.
+template <int DT, int T, int U, bool NT>
+__device__ __forceinline__ void step_tile_load_own(const RankPtrs& P, int n, StagedTile<U>& t) {
+  constexpr int V = Ops<DT>::V;
+  if (t.base >= t.hi) return;
+  const u32x4* dst = static_cast<const u32x4*>(P.p[wrap(t.r + 1, n)]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t vi = t.base / V + int64_t(u) * T + threadIdx.x;
+    if (vi * V >= t.lo && (vi + 1) * V <= t.hi) t.b[u] = ld16<NT>(dst + vi);
+  }
+}
+
+template <int DT, int T, int U, bool NT>
+__device__ __forceinline__ void step_tile_load(const RankPtrs& P, int n, int64_t count, int64_t L,
+                                               int64_t tiles_per_chunk, int64_t tile, int s, int phase,
+                                               StagedTile<U>& t) {
+  step_tile_place<DT, T, U>(n, count, L, tiles_per_chunk, tile, s, phase, t);
+  step_tile_load_sent<DT, T, U, NT>(P, t);
+  if (phase == DDP_RS) step_tile_load_own<DT, T, U, NT>(P, n, t);
+}
+
+template <int DT, int T, int U, bool NT>
+__device__ __forceinline__ void step_tile_finish(const RankPtrs& P, int n, int phase, const StagedTile<U>& t) {
+  using O = Ops<DT>;
+  constexpr int V = O::V;
+  if (t.base >= t.hi) return;
+  const void* src = P.p[t.r];
+  void* dst = P.p[wrap(t.r + 1, n)];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t vi = t.base / V + int64_t(u) * T + threadIdx.x;
+    if (vi * V >= t.lo && (vi + 1) * V <= t.hi) {
+      u32x4 y = t.a[u];
+      if (phase == DDP_RS) {
+        typename O::Acc acc = O::from(t.a[u]);
+        O::add(acc, t.b[u]);
+        y = O::to(acc);
+      }
+      st16<NT>(static_cast<u32x4*>(dst) + vi, y);
+    } else if ((vi + 1) * V > t.lo && vi * V < t.hi) {
+      // cut by a chunk boundary or the buffer's end: this chunk's elements only
+      const int64_t e0 = vi * V;
+      for (int64_t e = max(e0, t.lo); e < t.hi && e < e0 + V; ++e) {
+        const float x = O::load1(src, e);
+        O::store1(dst, e, phase == DDP_RS ? O::add1(x, O::load1(dst, e)) : x);
+      }
+    }
+  }
+}
+
 // Launch shape of the step kernels, measured on MI355X at 8 ranks: one wave
 // per block, one 16-byte vector per thread, one tile per block. When the N
 // buffers together exceed the 256 MB Infinity Cache the loads and stores are
@@ -143,36 +233,61 @@ __global__ __launch_bounds__(kStepThreads) void k_step(RankPtrs P, int n, int64_
 
 // ---------------------------------------------------------------- persistent
 
-// Word of a launch's barrier slot (64 words, zeroed before the launch) that
-// holds the tile-ticket counter: its own 128-byte line, away from the
-// arrival counter in word 0 that waiting blocks poll.
+// A launch's barrier slot (kSlotWords words, zeroed before the launch), one
+// 128-byte line per word in use:
+//   word 0:              arrivals over the whole launch; top bit: abort flag
+//   word kTicketWord:    the tile-ticket counter
+//   word kReleaseWord:   barriers completed; top bit: abort flag
+// Arriving blocks add to word 0 and only the last one of a barrier writes the
+// release word, which the waiting blocks poll: the polls never contend with
+// the arrivals' atomics on one line.
 constexpr int kTicketWord = 32;
+constexpr int kReleaseWord = 64;
 
-// Grid-wide barrier for a cooperative launch. counter[0] counts arrivals over
-// the whole launch; its top bit is the launch's abort flag. A block that has
-// waited longer than `deadline` wall-clock ticks sets the abort bit, records
-// what it saw in status[0..2] (timed out, arrivals seen, arrivals expected),
-// and every block then leaves. Returns false if the launch must stop.
-__device__ bool grid_barrier(unsigned int* counter, unsigned int target, unsigned int* status,
-                             unsigned long long deadline) {
-  __shared__ int ok;
+// Grid-wide barrier for a cooperative launch, in two halves so that a block
+// can issue loads that do not depend on the other blocks' writes (the next
+// reduce-scatter step's own operand) between its arrival and its wait.
+// Barrier number g (from 1) completes when g * gridDim.x + extra blocks have
+// arrived; `extra` is non-zero only when a test forces the time-out path.
+__device__ __forceinline__ void barrier_arrive(unsigned int* words, unsigned int target, unsigned int g) {
   __syncthreads();  // every wave of the block has issued its stores of the step
   if (threadIdx.x == 0) {
     // Release at agent scope (an L2 write-back on this part): the block's
     // writes become visible to every XCD before its arrival is counted.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    unsigned int seen = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const unsigned int prev = __hip_atomic_fetch_add(words, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1u == target) {
+      // The last arrival (never after an abort: the abort bit makes prev
+      // larger): it has seen every other block's arrival, so after an acquire
+      // it can release them all to the waiters. fetch_max keeps an abort bit.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_fetch_max(words + kReleaseWord, g, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Waits until barrier g is released. A block that has waited longer than
+// `deadline` wall-clock ticks sets the abort bit in words 0 and kReleaseWord,
+// records what it saw in status[0..2] (timed out, arrivals seen, arrivals
+// expected), and every block then leaves. Returns false if the launch must stop.
+__device__ __forceinline__ bool barrier_wait(unsigned int* words, unsigned int target, unsigned int g,
+                                             unsigned int* status, unsigned long long deadline) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) {
+    unsigned int* release = words + kReleaseWord;
+    unsigned int seen = __hip_atomic_load(release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long t0 = wall_clock64();
-    while ((seen & kAbortBit) == 0u && seen < target) {
-      __builtin_amdgcn_s_sleep(4);
-      seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((seen & kAbortBit) == 0u && seen < target && wall_clock64() - t0 > deadline) {
+    while ((seen & kAbortBit) == 0u && seen < g) {
+      __builtin_amdgcn_s_sleep(2);
+      seen = __hip_atomic_load(release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((seen & kAbortBit) == 0u && seen < g && wall_clock64() - t0 > deadline) {
         const unsigned int prev =
-            __hip_atomic_fetch_or(counter, kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(words, kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(release, kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_or(&status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_max(&status[1], prev & ~kAbortBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_max(&status[2], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        seen = prev | kAbortBit;
+        seen = kAbortBit;
       }
     }
     // Acquire at agent scope (a cache invalidate): the other blocks' writes
@@ -193,14 +308,16 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
                                                          unsigned int* counter, unsigned int* status,
                                                          unsigned long long deadline, unsigned int extra) {
   const int64_t total_tiles = int64_t(n) * tiles_per_chunk;
-  if constexpr (NT) {
+  if constexpr (NT && VEC) {
     // Tiles handed out by one ticket counter for the whole launch: tickets
     // [i * total, (i + 1) * total) are step i's tiles. A block takes its next
     // ticket while it works on the current tile; the one ticket past its
     // step that every block ends a step holding is a tile of the next step,
     // since the grid never exceeds one step's tiles. Thread 0 draws, and a
     // double-buffered LDS word passes the ticket to the block with one
-    // barrier per tile.
+    // barrier per tile. Between its arrival at a barrier and its wait, a
+    // block loads the own operand of that next tile if the next step is a
+    // reduce-scatter step.
     unsigned int* tickets = counter + kTicketWord;
     __shared__ unsigned int next_ticket[2];
     if (threadIdx.x == 0)
@@ -208,6 +325,8 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
     __syncthreads();
     unsigned int t = next_ticket[0];
     int k = 1;
+    StagedTile<kStepUnroll> cur;
+    bool own_loaded = false;  // cur holds the own operand of ticket t (loaded across a barrier)
     for (int i = 0; i < n_steps; ++i) {
       const int phase = i < n - 1 ? DDP_RS : DDP_AG;
       const int s = i < n - 1 ? i : i - (n - 1);
@@ -216,27 +335,80 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
         unsigned int drawn = 0u;
         if (threadIdx.x == 0)
           drawn = __hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk,
-                                                                int64_t(t) - int64_t(i) * total_tiles, s, phase);
+        if (own_loaded) {
+          step_tile_load_sent<DT, kPersistentThreads, kStepUnroll, NT>(P, cur);
+        } else {
+          step_tile_load<DT, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk,
+                                                                  int64_t(t) - int64_t(i) * total_tiles, s, phase,
+                                                                  cur);
+        }
+        own_loaded = false;
+        step_tile_finish<DT, kPersistentThreads, kStepUnroll, NT>(P, n, phase, cur);
         if (threadIdx.x == 0) next_ticket[k & 1] = drawn;
         __syncthreads();
         t = next_ticket[k & 1];
         ++k;
       }
-      if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
-        return;
+      if (i + 1 < n_steps) {
+        const unsigned int target = unsigned(i + 1) * gridDim.x + extra;
+        barrier_arrive(counter, target, unsigned(i + 1));
+        if (i + 1 < n - 1 && t < end + unsigned(total_tiles)) {  // the next step reduces: its own operand
+          step_tile_place<DT, kPersistentThreads, kStepUnroll>(n, count, L, tiles_per_chunk,
+                                                               int64_t(t) - int64_t(end), i + 1, DDP_RS, cur);
+          step_tile_load_own<DT, kPersistentThreads, kStepUnroll, NT>(P, n, cur);
+          own_loaded = true;
+        }
+        if (!barrier_wait(counter, target, unsigned(i + 1), status, deadline)) return;
+      }
     }
   } else {
     // Buffers inside the Infinity Cache: a fixed grid-stride share per block
     // (tickets measured 1-2 % slower here: 8 x 25 MiB 0.299-0.301 against
-    // 0.295-0.297 ms at 96 blocks).
+    // 0.295-0.297 ms at 96 blocks). With whole vectors, the next tile's loads
+    // are issued before the current tile's stores, so a block keeps two
+    // tiles' loads in flight, and between its arrival at a barrier and its
+    // wait it loads its first tile's own operand if the next step reduces.
+    bool own_loaded = false;
+    StagedTile<kStepUnroll> cur, nxt;
     for (int i = 0; i < n_steps; ++i) {
       const int phase = i < n - 1 ? DDP_RS : DDP_AG;
       const int s = i < n - 1 ? i : i - (n - 1);
-      for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
-        step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
-      if (i + 1 < n_steps && !grid_barrier(counter, unsigned(i + 1) * gridDim.x + extra, status, deadline))
-        return;
+      if constexpr (VEC) {
+        int64_t tile = blockIdx.x;
+        if (tile < total_tiles) {
+          if (own_loaded)
+            step_tile_load_sent<DT, kPersistentThreads, kStepUnroll, NT>(P, cur);
+          else
+            step_tile_load<DT, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s,
+                                                                    phase, cur);
+        }
+        own_loaded = false;
+        while (tile < total_tiles) {
+          const int64_t next = tile + gridDim.x;
+          if (next < total_tiles)
+            step_tile_load<DT, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, next, s,
+                                                                    phase, nxt);
+          step_tile_finish<DT, kPersistentThreads, kStepUnroll, NT>(P, n, phase, cur);
+          cur = nxt;
+          tile = next;
+        }
+      } else {
+        for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
+          step_tile<DT, VEC, kPersistentThreads, kStepUnroll, NT>(P, n, count, L, tiles_per_chunk, tile, s, phase);
+      }
+      if (i + 1 < n_steps) {
+        const unsigned int target = unsigned(i + 1) * gridDim.x + extra;
+        barrier_arrive(counter, target, unsigned(i + 1));
+        if constexpr (VEC) {
+          if (i + 1 < n - 1 && int64_t(blockIdx.x) < total_tiles) {  // the next step reduces: own operand
+            step_tile_place<DT, kPersistentThreads, kStepUnroll>(n, count, L, tiles_per_chunk, blockIdx.x, i + 1,
+                                                                 DDP_RS, cur);
+            step_tile_load_own<DT, kPersistentThreads, kStepUnroll, NT>(P, n, cur);
+            own_loaded = true;
+          }
+        }
+        if (!barrier_wait(counter, target, unsigned(i + 1), status, deadline)) return;
+      }
     }
   }
 }
@@ -244,12 +416,12 @@ __global__ __launch_bounds__(kPersistentThreads) void k_persistent(RankPtrs P, i
 // ---------------------------------------------------------------- allocation-free scratch
 
 // Barrier words of ring_allreduce_persistent_noalloc, for callers that cannot
-// allocate device memory: words [0, 64) are one launch's barrier slot
-// (arrivals in word 0, tile tickets in word kTicketWord), words [64, 67) its
-// sticky status (timed out, arrivals seen, arrivals expected). 512 bytes per
-// device, zero when the code object is loaded, held until the process ends.
-constexpr int kNoAllocSlotWords = 64;
-constexpr int kNoAllocWords = 128;
+// allocate device memory: words [0, 128) are one launch's barrier slot (the
+// layout above), words [128, 131) its sticky status (timed out, arrivals
+// seen, arrivals expected). 1 KiB per device, zero when the code object is
+// loaded, held until the process ends.
+constexpr int kNoAllocSlotWords = kSlotWords;
+constexpr int kNoAllocWords = 256;
 static __device__ __align__(256) unsigned int scratch[kNoAllocWords];
 
 // The device address of `scratch` on each device. In host code the array's
@@ -276,10 +448,11 @@ int noalloc_scratch(unsigned int** out) {
 
 // ---------------------------------------------------------------- host side
 
-// Tiles per chunk of the persistent kernel (256 threads x kStepUnroll vectors).
-template <int DT>
+// Tiles per chunk of the persistent kernel: 1024 threads x kStepUnroll
+// vectors, or x 1 element (buffers not 16-byte aligned).
+template <int DT, bool VEC>
 int64_t step_tiles_per_chunk(const RingArgs& a) {
-  const int64_t tile = step_vec(a) ? int64_t(kPersistentThreads) * kStepUnroll * Ops<DT>::V : kPersistentThreads;
+  const int64_t tile = VEC ? int64_t(kPersistentThreads) * kStepUnroll * Ops<DT>::V : int64_t(kPersistentThreads);
   return aligned_tiles_per_chunk(a.L, tile);
 }
 
@@ -343,7 +516,7 @@ struct PersistentOpts {
 // register limit, and the clamp is then one block per CU.)
 template <int DT, bool VEC, bool NT>
 int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* cus) {
-  const int64_t total = step_tiles_per_chunk<DT>(a) * a.n;
+  const int64_t total = step_tiles_per_chunk<DT, VEC>(a) * a.n;
   const void* fn = reinterpret_cast<const void*>(&k_persistent<DT, VEC, NT>);
   int dev = 0, per_cu = 0;
   DDP_HIP_TRY(hipGetDevice(&dev), "ring_allreduce_persistent: hipGetDevice");
@@ -356,13 +529,17 @@ int persistent_grid(const RingArgs& a, int32_t max_blocks, unsigned* grid, int* 
   const int64_t safe = int64_t(per_cu > 1 ? per_cu - 1 : 1) * (*cus);
   const int per8 = NT ? kPersistentBlocksPer8CUsStreaming : kPersistentBlocksPer8CUsCached;
   const int64_t want = max_blocks > 0 ? int64_t(max_blocks) : std::max<int64_t>(1, int64_t(per8) * (*cus) / 8);
-  *grid = unsigned(std::max<int64_t>(1, std::min({total, want, safe})));
+  int64_t g = std::max<int64_t>(1, std::min({total, want, safe}));
+  // A fixed share per block: as few blocks as give each block the same
+  // number of tiles per step (tickets balance the load by themselves).
+  if (!NT && max_blocks == 0) g = (total + (total + g - 1) / g - 1) / ((total + g - 1) / g);
+  *grid = unsigned(g);
   return DDP_OK;
 }
 
 template <int DT, bool VEC, bool NT>
 int launch_persistent_impl(const RingArgs& a, int n_steps, const PersistentOpts& o, hipStream_t s) {
-  const int64_t tpc = step_tiles_per_chunk<DT>(a);
+  const int64_t tpc = step_tiles_per_chunk<DT, VEC>(a);
   const void* fn = reinterpret_cast<const void*>(&k_persistent<DT, VEC, NT>);
   int dev = 0, clock_khz = 0, cus = 0;
   unsigned grid = 0;

@@ -81,8 +81,7 @@ bool all_aligned16(void* const* bufs, int32_t n) {
 namespace {
 
 constexpr int kSlots = 64;          // slots handed out round-robin per device
-constexpr int kSlotStride = 64;     // words between slots (256 bytes); a launch uses word 0 (barrier
-                                    // arrivals) and word 32 (the persistent kernel's tile tickets)
+constexpr int kSlotStride = kSlotWords;  // words between slots (512 bytes; the layout is in ring_kernels.hip)
 constexpr int kScratchWords = kSlots * kSlotStride + kSlotStride;  // + status line
 
 // HIP events for SlotRing: a slot's next user waits, on its own stream, for
