@@ -36,6 +36,8 @@ Usage:
                                     reduce-scatter (--dtype bf16 for bf16)
         c5  64 ranks x 300M fp32    variants: fused, steps, persistent,
                                     reduce-scatter
+        probe  the copy probe: 4 GiB read and 4 GiB written (variant: copy),
+               the same-run ceiling and the scale for traffic counters
       K timed steps after W untimed ones (--graph: replays of a HIP graph of
       one step, so no host work sits between its launches); prints one JSON
       line.
@@ -59,13 +61,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "ring_all_reduce_ddp_amd", "csrc", f)
                   for f in ("fused_kernels.hip", "ring_common.h", "hip_common.h")]
 
 CONFIGS = {"c1": "ring_n3_6", "c2": "ring_n8_25mib", "c3": "ddp_resnet50", "c4": "ring_n8_1gib",
-           "c5": "ring_n64_300m"}
+           "c5": "ring_n64_300m", "probe": "copy_probe_4gib"}
 VARIANTS = {
     "c1": ("fused", "steps", "persistent", "step"),
     "c2": ("fused", "steps", "persistent"),
     "c3": ("fused", "steps", "persistent", "view", "pack", "unpack", "allreduce", "bf16-fused", "bf16-view"),
     "c4": ("fused", "steps", "persistent", "reduce-scatter"),
     "c5": ("fused", "steps", "persistent", "reduce-scatter"),
+    "probe": ("copy",),
 }
 
 
@@ -76,7 +79,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", choices=["all", *CONFIGS], default="all",
                     help="one workload only (default: the whole benchmark)")
-    ap.add_argument("--variant", default=None, help="the form to time with --config (default: fused)")
+    ap.add_argument("--variant", default=None, help="the form to time with --config (default: fused; copy for probe)")
     ap.add_argument("--dtype", choices=["fp32", "bf16"], default="fp32", help="buffer dtype for --config c4")
     ap.add_argument("--graph", action="store_true",
                     help="with --config: time replays of a HIP graph of one step instead of eager calls")
@@ -85,7 +88,7 @@ def parse_args(argv=None):
         if args.variant is not None or args.dtype != "fp32" or args.graph:
             ap.error("--variant, --dtype and --graph need --config")
     else:
-        args.variant = args.variant or "fused"
+        args.variant = args.variant or VARIANTS[args.config][0]
         if args.variant not in VARIANTS[args.config]:
             ap.error(f"--variant {args.variant} is not one of {', '.join(VARIANTS[args.config])} "
                      f"for --config {args.config}")
@@ -283,10 +286,17 @@ def run_single(args):
 
     torch.cuda.set_device(0)
     cfg, variant, dtype = args.config, args.variant, args.dtype
-    w = WORKLOADS[CONFIGS[cfg]]
-    cfg_info = {"workload": w.name, "variant": variant}
+    cfg_info = {"workload": CONFIGS[cfg], "variant": variant}
+    w = WORKLOADS.get(CONFIGS[cfg])
     sync = None
-    if cfg == "c3":
+    if cfg == "probe":
+        src = torch.empty(1 << 30, dtype=torch.float32, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        n, S = 1, 4 << 30
+        fn = lambda: rar.ddp_copy_probe(dst, src)  # noqa: E731
+        hbm_bytes = 2 * S
+        cfg_info.update({"bytes_read": S, "bytes_written": S})
+    elif cfg == "c3":
         sync = ResNet50Sync(rar, torch, np)
         fn = sync.fn(variant)
         n, S = sync.n, sync.grad_bytes
@@ -320,7 +330,7 @@ def run_single(args):
     _, med, lo = time_each(fn, args.steps, torch)
     if variant == "persistent":
         rar.ddp_persistent_status()
-    bus = gbps(2 * (n - 1) / n * S, ms)
+    bus = gbps(2 * (n - 1) / n * S, ms) if cfg != "probe" else gbps(2 * S, ms)
     line = {"metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded)", "config": cfg_info,

@@ -44,10 +44,10 @@ def test_single_config_arguments_are_checked_before_any_gpu_work():
 def test_every_config_lists_its_forms():
     sys.path.insert(0, ROOT)
     import bench
-    assert set(bench.CONFIGS) == {"c1", "c2", "c3", "c4", "c5"}
+    assert set(bench.CONFIGS) == {"c1", "c2", "c3", "c4", "c5", "probe"}
     for cfg in bench.CONFIGS:
         args = bench.parse_args(["--config", cfg])
-        assert args.variant == "fused"
+        assert args.variant == ("copy" if cfg == "probe" else "fused")
         for v in bench.VARIANTS[cfg]:
             assert bench.parse_args(["--config", cfg, "--variant", v]).variant == v
     assert bench.parse_args([]).config == "all"
