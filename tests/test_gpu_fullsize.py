@@ -9,8 +9,10 @@
   rank must equal rank 0 bit for bit (torch's comparison); rank 0 is then
   compared, every element, with the oracle's closed-form ring-order sum of
   its chunk, computed one chunk column (N ranks x L elements) at a time from
-  a pristine copy of the inputs, so host memory stays bounded. The error
-  bound against the exact sum is checked on sampled positions.
+  a pristine copy of the inputs, so host memory stays bounded. The
+  reduce-scatter output (every rank's shard, scaled by fl32(1/N)) is checked
+  the same way, every element, against the same sums scaled and rounded once.
+  The error bound against the exact sum is checked on sampled positions.
 """
 
 import os
@@ -76,6 +78,15 @@ def every_element_check(w, dtype, variants=VARIANTS):
                               heavy_mult=w.heavy_mult)
     pristine = [b.clone() for b in bufs]
     ivt = INT_VIEW[dtype]
+    # the reduce-scatter output first: it reads the inputs and leaves them as they are
+    L = ring.chunk_length(count, n)
+    scale = float(np.float32(1) / np.float32(n))
+    shards = [torch.empty(min(L, count - c * L), dtype=bufs[0].dtype, device="cuda") for c in range(n)]
+    print(f"[{w.name} {dtype} reduce-scatter output] N={n} count={count}", flush=True)
+    rar.ring_reduce_scatter_fused(bufs, shards, scale)
+    torch.cuda.synchronize()
+    got_shards = [to_host(t, dtype) for t in shards]
+    del shards
     got = {}
     for i, variant in enumerate(variants):
         if i:
@@ -98,6 +109,8 @@ def every_element_check(w, dtype, variants=VARIANTS):
         want = oracle_chunk_sum(x, c, dtype)
         for variant in variants:
             assert_bit_equal(got[variant][lo:hi], want, f"{w.name} {dtype} {variant} chunk {c}")
+        shard = rounding.round_to(rounding.to_f64(want, dtype) * scale, dtype)
+        assert_bit_equal(got_shards[c], shard, f"{w.name} {dtype} reduce-scatter shard {c}")
     # every element lies within (N-1) u sum|g_i| of the exact sum (sampled:
     # the exact sum is an fsum per element)
     pos = sample_positions(count, n, 2000, seed=w.seed)

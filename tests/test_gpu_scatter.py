@@ -1,7 +1,7 @@
 """GPU parity of the reduce-scatter output (every rank's gradient shard)
 against the oracle's ring.reduce_scatter, bit for bit: small and ragged
-inputs at several N and both dtypes, and the 8 x 1 GiB and 64 x 300M
-workloads on sampled positions."""
+inputs at several N and both dtypes. (The 8 x 1 GiB and 64 x 300M workloads
+are compared every element in test_gpu_fullsize.py.)"""
 
 import numpy as np
 import pytest
@@ -9,7 +9,7 @@ import torch
 
 import ring_all_reduce_ddp_amd as rar
 from oracle import ring
-from ddp_workloads import WORKLOADS, host_ring_inputs, device_ring_inputs
+from ddp_workloads import host_ring_inputs
 
 from gpu_util import TORCH_DTYPE, to_device, to_host, assert_bit_equal
 
@@ -68,37 +68,3 @@ def test_overlapping_shard_refused():
     dev = to_device(host_ring_inputs(5, 2, 64, "fp32"), "fp32")
     with pytest.raises(rar.DDPError, match="overlaps bufs"):
         rar.ring_reduce_scatter_fused(dev, [dev[0][:32], dev[1][32:]])
-
-
-@pytest.mark.parametrize("name,dtype", [("ring_n8_1gib", "fp32"), ("ring_n8_1gib", "bf16"),
-                                        ("ring_n64_300m", "fp32")])
-def test_full_size_sampled(name, dtype):
-    """Full size: per chunk, k sampled positions from every rank form a small
-    ring whose chunks are the samples of the real chunks; the oracle's shards
-    of that small ring equal the GPU shards at those positions. 8 x 1 GiB in
-    both dtypes; 64 ranks x 300M fp32 (heavy-tailed values) takes the span
-    kernel."""
-    w = WORKLOADS[name]
-    count = w.count * (2 if dtype == "bf16" else 1)
-    n = w.n
-    bufs = device_ring_inputs(w.seed, n, count, dtype, std=w.std, heavy_frac=w.heavy_frac,
-                              heavy_mult=w.heavy_mult)
-    scale = float(np.float32(1) / np.float32(n))
-    L = count // n
-    k = 2048 if n <= 8 else 256
-    rng = np.random.default_rng(4)
-    offs = np.sort(np.concatenate([rng.choice(L, k - 4, replace=False), [0, 1, L - 2, L - 1]]))
-    offs = np.unique(offs)
-    k = len(offs)
-    pos = np.concatenate([c * L + offs for c in range(n)])
-    pos_dev = torch.from_numpy(pos).cuda()
-    mini = [to_host(t.index_select(0, pos_dev), dtype) for t in bufs]
-    shards = shard_buffers(count, n, dtype)
-    print(f"[reduce-scatter {name} {dtype}] samples per chunk={k}", flush=True)
-    rar.ring_reduce_scatter_fused(bufs, shards, scale)
-    torch.cuda.synchronize()
-    want = ring.reduce_scatter(mini, dtype, np.float32(scale))
-    offs_dev = torch.from_numpy(offs).cuda()
-    for c in range(n):
-        got = to_host(shards[c].index_select(0, offs_dev), dtype)
-        assert_bit_equal(got, want[c], f"{dtype} shard {c}")
