@@ -229,10 +229,11 @@ int ring_allreduce_persistent(void* const* bufs, int32_t N, int64_t count, int32
  * launch's knobs exposed:
  *   max_blocks: cooperative grid size (0: the default, 1024-thread blocks,
  *       seven for every eight compute units when the N buffers exceed the
- *       256 MB Infinity Cache, three for every eight when they fit); it is
- *       never more than one
- *       block per tile of a step, nor more than one block per compute unit
- *       below the occupancy limit (at least one per compute unit);
+ *       256 MB Infinity Cache; five for every eight when they fit, lowered
+ *       until every block has the same number of tiles per step); it is
+ *       never more than one block per tile of a step, nor more than one
+ *       block per compute unit below the occupancy limit (at least one per
+ *       compute unit);
  *   timeout_us: how long a block waits at a grid barrier before the launch
  *       gives up (ring_allreduce_persistent uses 10 s); in (0, 3600 s];
  *   extra_arrivals: added to every barrier's expected arrival count. It must

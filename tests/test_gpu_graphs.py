@@ -1,7 +1,7 @@
 """The library's launches captured in a HIP graph (torch.cuda.CUDAGraph on
 ROCm) and replayed: the copying DDP sync (pack, fused all-reduce, x1/N,
-unpack for every bucket), the in-place sync, the fused all-reduce and the
-2(N-1) step launches. Each graph is replayed several times, with the
+unpack for every bucket), the in-place sync, the fused all-reduce, the
+2(N-1) step launches and the allocation-free persistent all-reduce. Each graph is replayed several times, with the
 program's own eager work (restoring the inputs) and a synchronisation
 between replays, and every replay must equal the eager result bit for bit.
 The first call of a plan on a device makes its device tables, so one eager
@@ -102,3 +102,18 @@ def test_graph_of_ring_allreduce(variant, dtype):
     fn = (lambda: rar.ring_allreduce_fused(bufs)) if variant == "fused" else \
         (lambda: rar.ring_allreduce_stepwise(bufs))
     replay_matches_eager(bufs, pristine, fn, dtype, f"{variant} {dtype}")
+
+
+@pytest.mark.parametrize("count", [8 * 100_000 + 5, 8 * 1_000_000], ids=["cached", "tickets"])
+def test_graph_of_persistent_noalloc(count):
+    """The allocation-free persistent all-reduce (its barrier words cleared by
+    a fill kernel in the library's fixed array, then one cooperative launch)
+    captured and replayed; 8 x 1M fp32 (32 MiB per rank) exceeds the
+    Infinity Cache, so its tiles are handed out by tickets. A barrier time-out
+    in any replay would leave a sticky status, which the last call raises."""
+    n = 8
+    bufs = to_device(host_ring_inputs(36, n, count, "fp32", std=1e-2), "fp32")
+    pristine = [b.clone() for b in bufs]
+    replay_matches_eager(bufs, pristine, lambda: rar.ring_allreduce_persistent_noalloc(bufs), "fp32",
+                         f"persistent without allocation, {count} elements")
+    rar.ddp_persistent_status()
