@@ -28,8 +28,11 @@
  *     gradients and buckets share a dtype, the in-place sync's map of the
  *     gradient arena (2 bytes per 16 bytes of one rank's arena), made on the
  *     plan's first pack, unpack or in-place sync on that device and freed by
- *     ddp_plan_free; and per device, a few KiB of barrier and status words
- *     (kept until the process ends).
+ *     ddp_plan_free; and per device, the persistent launches' barrier
+ *     words (64 slots of 512 bytes plus a 512-byte status line, 32.5 KiB,
+ *     allocated on the first persistent call on that device) and the
+ *     allocation-free entry point's fixed 1 KiB array, both kept until the
+ *     process ends.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     and the call returns without waiting; completion follows stream order,
  *     the analogue of waiting on the collective's work handle ([D], "源码阅读路线").
