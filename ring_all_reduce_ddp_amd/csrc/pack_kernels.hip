@@ -115,7 +115,12 @@ __global__ __launch_bounds__(kThreads) void k_unpack_scale(const Segment* segs, 
 
 // fp32 gradients into a bf16 bucket (the bf16 compression hook): every
 // gradient is rounded to the nearest bf16, ties to even. A bucket vector is 8
-// bf16 elements; it reads two 16-byte vectors of fp32 gradients.
+// bf16 elements; it reads two 16-byte vectors of fp32 gradients. NTL as in
+// k_pack: streaming the gradients keeps the bucket in the Infinity Cache for
+// the all-reduce (compressed ResNet-50 sync over 8 ranks: 0.589 against
+// 0.658 ms with cached loads, although the packs alone took 0.243 against
+// 0.237 ms).
+template <bool NTL>
 __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* segs, const int32_t* tile_seg, int64_t n_tiles,
                                                                RankPtrs arenas, RankPtrs buckets) {
   constexpr int V = 8;
@@ -132,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void k_pack_f32_to_bf16(const Segment* se
       const int64_t e = first + (int64_t(u) * kThreads + threadIdx.x) * V;
       if (e + V <= sg.numel) {
         const u32x4* src = reinterpret_cast<const u32x4*>(arena + sg.src_off + e);
-        a[u] = src[0];
-        b[u] = src[1];
+        a[u] = ld16<NTL>(src);
+        b[u] = ld16<NTL>(src + 1);
       }
     }
 #pragma unroll
@@ -306,7 +311,10 @@ extern "C" int bucket_pack(const ddp_plan* plan, int32_t b, const void* const* g
   const int32_t* ts = tile_seg + bk.tile_seg_begin;
   const bool ntl = int64_t(N) * plan->arena_numel * elem_bytes(plan->dtype) > kInfinityCacheBytes;
   if (plan->dtype != plan->comm_dtype) {
-    hipLaunchKernelGGL(k_pack_f32_to_bf16, g, blk, 0, s, sg, ts, bk.n_tiles, A, B);
+    if (ntl)
+      hipLaunchKernelGGL(k_pack_f32_to_bf16<true>, g, blk, 0, s, sg, ts, bk.n_tiles, A, B);
+    else
+      hipLaunchKernelGGL(k_pack_f32_to_bf16<false>, g, blk, 0, s, sg, ts, bk.n_tiles, A, B);
   } else if (plan->dtype == DDP_FP32) {
     if (ntl)
       hipLaunchKernelGGL((k_pack<DDP_FP32, true>), g, blk, 0, s, sg, ts, bk.n_tiles, A, B);
