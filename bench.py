@@ -27,17 +27,22 @@ Usage:
   python bench.py --config c1|c2|c3|c4|c5 [--variant V] [--dtype fp32|bf16]
                   [--graph] [--steps K] [--warmup W]
       one workload and one form only (for profiling a single kernel):
-        c1  3 ranks x 6 elements    variants: fused, steps, persistent, step
-        c2  8 ranks x 25 MiB        variants: fused, steps, persistent
+        c1  3 ranks x 6 elements    variants: fused, steps, persistent,
+                                    persistent-noalloc, step
+        c2  8 ranks x 25 MiB        variants: fused, steps, persistent,
+                                    persistent-noalloc
         c3  ResNet-50 DDP sync, 8   variants: fused, steps, persistent, view,
                                     pack, unpack, allreduce, bf16-fused,
                                     bf16-view
         c4  8 ranks x 1 GiB         variants: fused, steps, persistent,
-                                    reduce-scatter (--dtype bf16 for bf16)
+                                    persistent-noalloc, reduce-scatter
+                                    (--dtype bf16 for bf16)
         c5  64 ranks x 300M fp32    variants: fused, steps, persistent,
-                                    reduce-scatter
+                                    persistent-noalloc, reduce-scatter
         probe  the copy probe: 4 GiB read and 4 GiB written (variant: copy),
                the same-run ceiling and the scale for traffic counters
+      persistent-noalloc is the allocation-free entry point, which --graph can
+      capture; the persistent form itself is timed eagerly.
       K timed steps after W untimed ones (--graph: replays of a HIP graph of
       one step, so no host work sits between its launches); prints one JSON
       line.
@@ -63,11 +68,11 @@ KERNEL_SOURCES = [os.path.join(ROOT, "ring_all_reduce_ddp_amd", "csrc", f)
 CONFIGS = {"c1": "ring_n3_6", "c2": "ring_n8_25mib", "c3": "ddp_resnet50", "c4": "ring_n8_1gib",
            "c5": "ring_n64_300m", "probe": "copy_probe_4gib"}
 VARIANTS = {
-    "c1": ("fused", "steps", "persistent", "step"),
-    "c2": ("fused", "steps", "persistent"),
+    "c1": ("fused", "steps", "persistent", "persistent-noalloc", "step"),
+    "c2": ("fused", "steps", "persistent", "persistent-noalloc"),
     "c3": ("fused", "steps", "persistent", "view", "pack", "unpack", "allreduce", "bf16-fused", "bf16-view"),
-    "c4": ("fused", "steps", "persistent", "reduce-scatter"),
-    "c5": ("fused", "steps", "persistent", "reduce-scatter"),
+    "c4": ("fused", "steps", "persistent", "persistent-noalloc", "reduce-scatter"),
+    "c5": ("fused", "steps", "persistent", "persistent-noalloc", "reduce-scatter"),
     "probe": ("copy",),
 }
 
@@ -95,7 +100,8 @@ def parse_args(argv=None):
         if args.dtype == "bf16" and args.config != "c4":
             ap.error("--dtype bf16 is available for --config c4 only")
         if args.graph and args.variant == "persistent":
-            ap.error("--graph: the persistent form orders its barrier words with events; time it eagerly")
+            ap.error("--graph: the persistent form orders its barrier words with events; time it eagerly "
+                     "(or capture persistent-noalloc)")
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
     return args
@@ -190,7 +196,7 @@ def ring_bytes(variant, n, S):
     writes S; one reduce-scatter step reads 2S and writes S."""
     if variant == "fused":
         return 2 * n * S
-    if variant in ("steps", "persistent"):
+    if variant in ("steps", "persistent", "persistent-noalloc"):
         return 5 * (n - 1) * S
     if variant == "reduce-scatter":
         return (n + 1) * S
@@ -206,6 +212,8 @@ def ring_step_fn(rar, variant, bufs, shards=None, scale=1.0):
         return lambda: rar.ring_allreduce_stepwise(bufs)
     if variant == "persistent":
         return lambda: rar.ring_allreduce_persistent(bufs)
+    if variant == "persistent-noalloc":
+        return lambda: rar.ring_allreduce_persistent_noalloc(bufs)
     if variant == "step":
         return lambda: rar.ring_allreduce_step(bufs, 0, rar.DDP_RS)
     if variant == "reduce-scatter":
@@ -328,7 +336,7 @@ def run_single(args):
         fn()
     ms = time_launches(fn, args.steps, torch)
     _, med, lo = time_each(fn, args.steps, torch)
-    if variant == "persistent":
+    if variant.startswith("persistent"):
         rar.ddp_persistent_status()
     bus = gbps(2 * (n - 1) / n * S, ms) if cfg != "probe" else gbps(2 * S, ms)
     line = {"metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

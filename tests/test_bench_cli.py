@@ -55,6 +55,10 @@ def test_every_config_lists_its_forms():
     assert bench.ring_bytes("fused", 8, 1 << 30) == 16 << 30
     assert bench.ring_bytes("steps", 8, 1 << 30) == 35 << 30
     assert bench.ring_bytes("reduce-scatter", 8, 1 << 30) == 9 << 30
+    assert bench.ring_bytes("persistent-noalloc", 8, 1 << 30) == bench.ring_bytes("persistent", 8, 1 << 30)
+    # the allocation-free persistent entry point is the one form of it that a graph can hold
+    for cfg in ("c1", "c2", "c4", "c5"):
+        assert bench.parse_args(["--config", cfg, "--variant", "persistent-noalloc", "--graph"]).graph
 
 
 def test_traffic_figure_follows_the_kernel_sources():
