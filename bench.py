@@ -11,7 +11,8 @@ CPU oracle's hop-by-hop ring on the same inputs (`parity`).
 
 Beside it, in the same run: the step-by-step and persistent forms, the
 reduce-scatter output alone, the same inputs in one allocation with the ranks
-offset by 4 KiB, and the bf16 buffers of the same workload, the
+offset by 4 KiB and in physically contiguous memory from the library's
+allocator, and the bf16 buffers of the same workload, the
 launch cost of the pages' 3-rank example, one default-size DDP bucket
 (8 x 25 MiB, cache-resident, and again with the cache flushed before each
 launch) in all three forms, a copy probe, the whole DDP sync of ResNet-50
@@ -221,6 +222,25 @@ def ring_step_fn(rar, variant, bufs, shards=None, scale=1.0):
     raise ValueError(variant)
 
 
+def contiguous_copies(rar, torch, tensors):
+    """Copies of equal-length fp32 tensors in physically contiguous memory
+    from the library's allocator, one allocation each: (allocations, views),
+    or (None, message) if the memory cannot be had."""
+    mems = []
+    try:
+        for t in tensors:
+            mems.append(rar.device_alloc(t.numel() * t.element_size(), contiguous=True))
+    except rar.DDPError as e:
+        for m in mems:
+            m.free()
+        return None, str(e)
+    views = [m.tensor(t.dtype, t.numel()) for m, t in zip(mems, tensors)]
+    for v, t in zip(views, tensors):
+        v.copy_(t)
+    torch.cuda.synchronize()
+    return mems, views
+
+
 class ResNet50Sync:
     """The ResNet-50 DDP sync over 8 ranks: plan, gradient arenas drawn on the
     GPU, bucket buffers (fp32, and bf16 for the compression hook)."""
@@ -398,8 +418,22 @@ def run_all(args):
     del shards5
     n64["fused_on_first_allocation"] = n64_first
     rar.ddp_persistent_status()
+    # The same values in physically contiguous memory from the library's
+    # allocator: the slow first-allocation case above spends more time in
+    # second-level address translation per request.
+    del first
+    torch.cuda.empty_cache()
+    mems, views = contiguous_copies(rar, torch, b5)
+    if mems is None:
+        n64["fused_on_contiguous_allocation"] = {"error": views}
+    else:
+        n64["fused_on_contiguous_allocation"] = n64_time(lambda: rar.ring_allreduce_fused(views),
+                                                         2 * w5.n * S5, 1)
+        del views
+        for m in mems:
+            m.free()
     extras["ring_n64_300m"] = n64
-    del b5, first
+    del b5
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ headline: fused, N=8, 1 GiB fp32
@@ -462,9 +496,9 @@ def run_all(args):
     # 1 GiB allocations start 2 MiB apart, so every block's 8 loads of one
     # offset agree in their low 21 address bits; offsets between the ranks
     # that are not multiples of 8 KiB ran faster at this size (multiples of
-    # 8 KiB did not), which points at DRAM bank conflicts. Reported beside
-    # the headline, which keeps the separate allocations a caller would
-    # normally hand over.
+    # 8 KiB up to 128 KiB did not), which points at DRAM bank conflicts.
+    # Reported beside the headline, which keeps the separate allocations a
+    # caller would normally hand over.
     pad = 4096 // 4
     arena = torch.empty(n * (count + pad), device="cuda")
     views = [arena[r * (count + pad): r * (count + pad) + count] for r in range(n)]
@@ -477,8 +511,24 @@ def run_all(args):
         "ms": round(t, 4), "hbm_gbps": round(gbps(2 * n * S, t), 1),
         "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4),
         "rank_stride_bytes": (count + pad) * 4}
+    # The same inputs again, each rank in physically contiguous memory from the
+    # library's allocator (ddp_device_alloc): less second-level address
+    # translation per access than torch's allocations.
+    mems, cviews = contiguous_copies(rar, torch, views)
     del arena, views
     torch.cuda.empty_cache()
+    if mems is None:
+        extras["contiguous_allocation"] = {"error": cviews}
+    else:
+        rar.ring_allreduce_fused(cviews)
+        t = time_launches(lambda: rar.ring_allreduce_fused(cviews), reps, torch)
+        extras["contiguous_allocation"] = {
+            "ms": round(t, 4), "hbm_gbps": round(gbps(2 * n * S, t), 1),
+            "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4),
+            "buffers": "one physically contiguous allocation per rank (ddp_device_alloc)"}
+        del cviews
+        for m in mems:
+            m.free()
 
     bb = device_ring_inputs(w.seed, n, 2 * count, "bf16", std=w.std)
     rar.ring_allreduce_fused(bb)

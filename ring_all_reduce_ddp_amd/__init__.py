@@ -89,6 +89,8 @@ def _load():
         "ddp_synthetic_backward_pass": (ctypes.c_int, [vp, pp, pp, i32, i32, i32, vp, vp]),
         "ddp_count_mismatches": (ctypes.c_int, [pp, i32, i64, i32, vp, vp]),
         "ddp_copy_probe": (ctypes.c_int, [vp, vp, i64, vp]),
+        "ddp_device_alloc": (ctypes.c_int, [i64, i32, ctypes.POINTER(vp)]),
+        "ddp_device_free": (ctypes.c_int, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -432,6 +434,60 @@ def ddp_count_mismatches(bufs, out, count=None, dtype=None, stream=None):
     """Enqueues the count into `out` (a device int64/uint64 tensor of one element)."""
     ptrs, n, count, dt = _ring_args(bufs, count, dtype)
     _check(_get_lib().ddp_count_mismatches(ptrs, n, count, dt, ctypes.c_void_p(_ptr(out)), _stream(stream)))
+
+
+DDP_ALLOC_CONTIGUOUS = 1
+
+_TORCH_TYPESTR = {torch.float32: "<f4", torch.bfloat16: "<V2", torch.uint8: "|u1"}
+
+
+class DeviceBuffer:
+    """Device memory from ddp_device_alloc, owned by this object (freed by
+    free() or when it is collected). `ptr` is the device address; tensor()
+    gives a torch view of it (the buffer must outlive the view)."""
+
+    def __init__(self, ptr, nbytes, contiguous):
+        self.ptr = ptr
+        self.nbytes = nbytes
+        self.contiguous = contiguous
+
+    def tensor(self, dtype=torch.float32, numel=None, offset_bytes=0):
+        """A 1-D tensor of `numel` elements at ptr + offset_bytes (no copy)."""
+        esize = torch.empty((), dtype=dtype).element_size()
+        if numel is None:
+            numel = (self.nbytes - offset_bytes) // esize
+        if self.ptr is None or offset_bytes < 0 or offset_bytes % esize or offset_bytes + numel * esize > self.nbytes:
+            raise ValueError("the view does not fit in the buffer")
+        # bfloat16 has no array-interface type string: view the bytes, then reinterpret
+        view_dtype = dtype if dtype in (torch.float32, torch.uint8) else torch.uint8
+        n = numel if view_dtype is dtype else numel * esize
+
+        class _Iface:
+            __cuda_array_interface__ = {"shape": (n,), "typestr": _TORCH_TYPESTR[view_dtype],
+                                        "data": (self.ptr + offset_bytes, False), "version": 2}
+        t = torch.as_tensor(_Iface(), device=torch.device("cuda", torch.cuda.current_device()))
+        return t if view_dtype is dtype else t.view(dtype)
+
+    def free(self):
+        if self.ptr is not None:
+            _check(_get_lib().ddp_device_free(ctypes.c_void_p(self.ptr)))
+            self.ptr = None
+
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if _finalizing():
+            return
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def device_alloc(nbytes, contiguous=True):
+    """nbytes of device memory on the current device (ddp_device_alloc);
+    contiguous=True asks for physically contiguous memory."""
+    p = ctypes.c_void_p()
+    _check(_get_lib().ddp_device_alloc(int(nbytes), DDP_ALLOC_CONTIGUOUS if contiguous else 0, ctypes.byref(p)))
+    return DeviceBuffer(p.value, int(nbytes), bool(contiguous))
 
 
 def ddp_copy_probe(dst, src, nbytes=None, stream=None):

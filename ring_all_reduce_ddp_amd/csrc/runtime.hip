@@ -363,6 +363,33 @@ extern "C" int ddp_count_mismatches(void* const* bufs, int32_t N, int64_t count,
   return DDP_OK;
 }
 
+extern "C" int ddp_device_alloc(int64_t nbytes, int32_t flags, void** out) {
+  const char* fn = "ddp_device_alloc";
+  if (out == nullptr) return fail(DDP_EINVAL, std::string(fn) + ": out is NULL");
+  *out = nullptr;
+  if (nbytes <= 0) return fail(DDP_EINVAL, std::string(fn) + ": nbytes must be positive");
+  if (flags != 0 && flags != DDP_ALLOC_CONTIGUOUS)
+    return fail(DDP_EINVAL, std::string(fn) + ": flags must be 0 or DDP_ALLOC_CONTIGUOUS");
+  void* p = nullptr;
+  const hipError_t e = flags == DDP_ALLOC_CONTIGUOUS
+                           ? hipExtMallocWithFlags(&p, size_t(nbytes), hipDeviceMallocContiguous)
+                           : hipMalloc(&p, size_t(nbytes));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DDP_ENOMEM, std::string(fn) + ": " + std::to_string(nbytes) + " bytes" +
+                                (flags == DDP_ALLOC_CONTIGUOUS ? " of contiguous memory" : "") + ": " +
+                                hipGetErrorString(e));
+  }
+  *out = p;
+  return DDP_OK;
+}
+
+extern "C" int ddp_device_free(void* p) {
+  if (p == nullptr) return DDP_OK;
+  DDP_HIP_TRY(hipFree(p), "ddp_device_free: hipFree");
+  return DDP_OK;
+}
+
 extern "C" int ddp_copy_probe(void* dst, const void* src, int64_t nbytes, void* stream) {
   const char* fn = "ddp_copy_probe";
   if (nbytes < 0 || nbytes % 16 != 0)

@@ -311,3 +311,18 @@ def test_arena_map_errors():
     pc = rar.ddp_bucket_plan_ex([4, 8], "fp32", "bf16", world_size=2)
     assert lib.ddp_plan_arena_map(pc.handle, out, 3) == rar.DDP_OK   # the compressed plan's fp32 arena
     expect_status(lib.ddp_plan_arena_map(pc.handle, out, 4), rar.DDP_EINVAL, "vector count")
+
+
+def test_device_alloc_argument_errors():
+    """ddp_device_alloc refuses a non-positive size, an unknown flag and a
+    NULL out before calling the HIP runtime; freeing NULL is a no-op."""
+    import ctypes
+    lib = rar.lib
+    out = ctypes.c_void_p(1234)
+    for nbytes, flags, msg in ((0, 0, "nbytes must be positive"), (-16, 1, "nbytes must be positive"),
+                               (64, 2, "flags must be 0 or DDP_ALLOC_CONTIGUOUS")):
+        assert lib.ddp_device_alloc(nbytes, flags, ctypes.byref(out)) == rar.DDP_EINVAL
+        assert msg in lib.ddp_last_error().decode()
+        assert out.value is None
+    assert lib.ddp_device_alloc(64, 0, None) == rar.DDP_EINVAL
+    assert lib.ddp_device_free(None) == rar.DDP_OK
