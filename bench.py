@@ -222,6 +222,17 @@ def ring_step_fn(rar, variant, bufs, shards=None, scale=1.0):
     raise ValueError(variant)
 
 
+def add_copy_fraction(node, copy_gbps):
+    """Adds hbm_frac_of_copy_probe beside every hbm_gbps figure in a nested
+    dict of results (the copy probe itself excepted)."""
+    if isinstance(node, dict):
+        hbm = node.get("hbm_gbps", node.get("hbm_gbps_algorithmic"))
+        if isinstance(hbm, (int, float)) and "bytes_moved" not in node:
+            node["hbm_frac_of_copy_probe"] = round(hbm / copy_gbps, 4)
+        for v in node.values():
+            add_copy_fraction(v, copy_gbps)
+
+
 def contiguous_copies(rar, torch, tensors):
     """Copies of equal-length fp32 tensors in physically contiguous memory
     from the library's allocator, one allocation each: (allocations, views),
@@ -730,6 +741,9 @@ def run_all(args):
            "sample": (f"the whole workload (8 ranks x {count} fp32, the same bytes the GPU reduced), "
                       f"hop-by-hop numpy simulation with single-threaded ufuncs: {cpu_s:.2f} s"),
            "host_cpus_available": len(os.sched_getaffinity(0))}
+
+    # every other workload's HBM rate also against the same run's copy probe
+    add_copy_fraction(extras, extras["copy_probe"]["gbps"])
 
     line = {
         "metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1,

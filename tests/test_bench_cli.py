@@ -81,3 +81,16 @@ def test_traffic_figure_follows_the_kernel_sources():
     else:
         assert traffic is None
     assert sorted(os.path.join(ROOT, s) for s in prof["kernel_sources"]) == sorted(bench.KERNEL_SOURCES)
+
+
+def test_copy_fraction_is_added_beside_every_hbm_rate():
+    sys.path.insert(0, ROOT)
+    import bench
+    extras = {"copy_probe": {"bytes_moved": 8, "ms": 1.0, "gbps": 6000.0, "hbm_gbps": 6000.0},
+              "steps": {"hbm_gbps": 6600.0},
+              "sync": {"view": {"hbm_gbps_algorithmic": 3000.0}, "plain": {"ms": 1.0}}}
+    bench.add_copy_fraction(extras, 6000.0)
+    assert extras["steps"]["hbm_frac_of_copy_probe"] == 1.1
+    assert extras["sync"]["view"]["hbm_frac_of_copy_probe"] == 0.5
+    assert "hbm_frac_of_copy_probe" not in extras["sync"]["plain"]
+    assert "hbm_frac_of_copy_probe" not in extras["copy_probe"]
