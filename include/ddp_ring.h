@@ -441,7 +441,7 @@ int ddp_count_mismatches(void* const* bufs, int32_t N, int64_t count, int32_t dt
  * the 64 ranks x 300M fused all-reduce ran 25.0-25.2 ms on such buffers
  * whether they were a process's first allocations or not, where torch's
  * first allocations ran up to 29.7 ms on some machines (more second-level
- * address translation per request); at 8 ranks x 1 GiB it ran within 3 %
+ * address translation per request); at 8 ranks x 1 GiB it ran within 5 %
  * of torch's allocations, faster or slower from run to run. Returns
  * DDP_EINVAL for nbytes <= 0, an
  * unknown flag or a NULL out (*out is set to NULL on every failure), and
