@@ -21,6 +21,11 @@ tests/test_oracle_*.py.  Parity status per function:
   ring.ring_simulate                     : pinned (worked example, integer
       brute force, association-order fixtures, invariants, error bound)
   ring.ring_order_sum                    : pinned (association-order fixtures)
+  ring.error_bound / abs_sum_f64, rounding.unit_roundoff
+                                         : pinned (hand-derived bound cases in
+      which the bound is reached, numpy's and torch's spacing above 1, fsum)
+  ring.reduce_scatter                    : pinned (integer shards, closed-form
+      ring-order sums of each chunk)
   planner.plan                           : pinned on constants, invariants and
       hand-derived plans; the exact ResNet-50 split depends on the reading of
       "capacity" and is parity unpinned by the pages

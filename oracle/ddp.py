@@ -13,7 +13,7 @@ What it follows:
     each bucket's all-reduce completes, the bucket is divided by the world size
     and copied back into the parameters' gradients.
 
-Readings (listed in the design notes): the division by N is a multiplication
+Readings where the pages leave a step open: the division by N is a multiplication
 by the fp32 value scale = fl(1/N), rounded once to the buffer dtype; for N a
 power of two this is exactly the division.  Buckets are processed in plan
 order, one after the other.

@@ -19,7 +19,7 @@ What it follows:
     (r-s) mod N.  The section 03 page says every other convention is a global
     shift with the same traffic; parity is defined against this one.
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent:
   * chunk length L = ceil(count / N); chunk c covers [c*L, min((c+1)*L, count))
     and may be short or empty when N does not divide count;
   * every hop rounds once to the buffer dtype (see rounding.py);

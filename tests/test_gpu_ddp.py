@@ -282,7 +282,7 @@ def test_bf16_compression_rounding_on_bit_patterns():
     does, on 2^22 random fp32 bit patterns (every exponent, subnormals, NaNs,
     infinities) plus hand-picked halfway, overflow and subnormal cases. NaNs
     are compared by position only: the oracle's NaN is canonical, the
-    kernel keeps the payload's upper bits (reading 4 of the design notes)."""
+    kernel keeps the payload's upper bits with the quiet bit set."""
     edge = np.array([0x00000000, 0x80000000, 0x00000001, 0x00008000, 0x00018000, 0x007fffff,
                      0x00807fff, 0x00808000, 0x00818000, 0x3f808000, 0x3f818000, 0x3f807fff,
                      0x7f7f7fff, 0x7f7f8000, 0x7f7fffff, 0xff7fffff, 0x7f800000, 0xff800000,
