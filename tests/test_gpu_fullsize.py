@@ -12,7 +12,9 @@
   a pristine copy of the inputs, so host memory stays bounded. The
   reduce-scatter output (every rank's shard, scaled by fl32(1/N)) is checked
   the same way, every element, against the same sums scaled and rounded once.
-  The error bound against the exact sum is checked on sampled positions.
+  Every element also lies within the error bound (N-1) u sum|g_i| of the
+  fp64 sum of the inputs (the bound widened by 2^-20 for the fp64 rounding),
+  and within the bound of the exact sum on sampled positions.
 """
 
 import os
@@ -71,6 +73,27 @@ def oracle_chunk_sum(x, c, dtype):
     return out
 
 
+def bound_holds_everywhere(x, got, dtype):
+    """Every element of `got` (an (N, k) chunk column's result) lies within
+    (N-1) u sum|g_i| of the sum of the N inputs, with the sum and sum|g_i|
+    taken in fp64 (not exactly: their own rounding errors, at most about
+    N 2^-53 relative, are covered by widening the bound by a factor 1 + 2^-20,
+    far below what a wrong unit roundoff or term count would need). Computed
+    in pieces of 2^20 positions on a thread pool, like oracle_chunk_sum."""
+    n, k = x.shape
+    tol_factor = (n - 1) * rounding.unit_roundoff(dtype) * (1 + 2.0 ** -20)
+    piece = 1 << 20
+
+    def run(a):
+        b = min(a + piece, k)
+        xs = rounding.to_f64(x[:, a:b], dtype)
+        err = np.abs(rounding.to_f64(got[a:b], dtype) - xs.sum(axis=0))
+        return bool(np.all(err <= tol_factor * np.abs(xs).sum(axis=0)))
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        return all(ex.map(run, range(0, k, piece)))
+
+
 def every_element_check(w, dtype, variants=VARIANTS):
     n = w.n
     count = elements_for(w, dtype)
@@ -111,8 +134,8 @@ def every_element_check(w, dtype, variants=VARIANTS):
             assert_bit_equal(got[variant][lo:hi], want, f"{w.name} {dtype} {variant} chunk {c}")
         shard = rounding.round_to(rounding.to_f64(want, dtype) * scale, dtype)
         assert_bit_equal(got_shards[c], shard, f"{w.name} {dtype} reduce-scatter shard {c}")
-    # every element lies within (N-1) u sum|g_i| of the exact sum (sampled:
-    # the exact sum is an fsum per element)
+        assert bound_holds_everywhere(x, got[variants[0]][lo:hi], dtype), f"{w.name} {dtype} chunk {c}: error bound"
+    # and against the exact sum (an fsum per element) on sampled positions
     pos = sample_positions(count, n, 2000, seed=w.seed)
     pos_dev = torch.from_numpy(pos).cuda()
     before = [gather(p, pos_dev, dtype) for p in pristine]
