@@ -86,3 +86,30 @@ def test_noalloc_argument_errors():
     assert "n_steps" in lib.ddp_last_error().decode()
     assert lib.ring_allreduce_persistent_noalloc(bufs, 2, 10, rar.DDP_FP32, 2, None) == rar.DDP_EINVAL
     assert "device allocation" in lib.ddp_last_error().decode()
+
+
+def test_noalloc_timeout_is_reported_once():
+    """The time-out path of the allocation-free launch, forced from the host
+    (every barrier expects one block more than the grid holds, and gives up
+    after 20 ms): every block exits, ddp_persistent_status reports it from the
+    fixed array's status words once, and the next call is exact."""
+    n, count = 4, 4 * 8192
+    host = host_ring_inputs(80, n, count, "fp32")
+    bufs = to_device(host, "fp32")
+    print("[noalloc time-out] forced with the test hook", flush=True)
+    rar.ddp_persistent_test_hook(1, 20_000)
+    try:
+        noalloc(bufs, "fp32")
+        torch.cuda.synchronize()
+    finally:
+        rar.ddp_persistent_test_hook(0, 0)
+    with pytest.raises(rar.DDPError, match="timed out"):
+        rar.ddp_persistent_status()
+    rar.ddp_persistent_status()  # cleared
+    bufs = to_device(host, "fp32")
+    noalloc(bufs, "fp32")
+    torch.cuda.synchronize()
+    rar.ddp_persistent_status()
+    want = ring.ring_simulate(host, "fp32")["bufs"]
+    for r in range(n):
+        assert_bit_equal(to_host(bufs[r], "fp32"), want[r], f"after the time-out, rank {r}")
