@@ -11,8 +11,9 @@ CPU oracle's hop-by-hop ring on the same inputs (`parity`).
 
 Beside it, in the same run: the step-by-step and persistent forms, the
 reduce-scatter output alone, the same inputs in one allocation with the ranks
-offset by 4 KiB and in physically contiguous memory from the library's
-allocator, and the bf16 buffers of the same workload, the
+offset by 4 KiB, in separate allocations with rank r starting r * 4 KiB into
+its own, and in physically contiguous memory from the library's allocator,
+and the bf16 buffers of the same workload, the
 launch cost of the pages' 3-rank example, one default-size DDP bucket
 (8 x 25 MiB, cache-resident, and again with the cache flushed before each
 launch) in all three forms, a copy probe, the whole DDP sync of ResNet-50
@@ -522,6 +523,27 @@ def run_all(args):
         "ms": round(t, 4), "hbm_gbps": round(gbps(2 * n * S, t), 1),
         "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4),
         "rank_stride_bytes": (count + pad) * 4}
+    # The same inputs in separate allocations from the library's allocator,
+    # rank r's buffer starting r * 4 KiB into its own allocation, so that the
+    # ranks' same-position accesses differ in their low address bits as in one
+    # allocation, without carving the ranks from one block.
+    offs = []
+    for r in range(n):
+        m = rar.device_alloc(S + r * 4096, contiguous=False)
+        v = m.tensor(torch.float32, count, offset_bytes=r * 4096)
+        v.copy_(views[r])
+        offs.append((m, v))
+    ov = [v for _, v in offs]
+    rar.ring_allreduce_fused(ov)
+    t = time_launches(lambda: rar.ring_allreduce_fused(ov), reps, torch)
+    extras["layout_rank_offsets_4kib"] = {
+        "ms": round(t, 4), "hbm_gbps": round(gbps(2 * n * S, t), 1),
+        "hbm_frac_of_peak": round(gbps(2 * n * S, t) / PEAK_HBM_GBPS, 4),
+        "buffers": "one allocation per rank (ddp_device_alloc), rank r starting r * 4 KiB into it"}
+    del ov
+    for m, _ in offs:
+        m.free()
+    del offs
     # The same inputs again, each rank in physically contiguous memory from the
     # library's allocator (ddp_device_alloc): less second-level address
     # translation per access than torch's allocations.
